@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: the forward
+(fa_fwd) and the backward (preprocess, main, postprocess) on the same stream.  Inputs,
+outputs and workspace are allocated and resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout:
+  value           whole-step attention TFLOP/s (fwd+bwd algorithmic FLOPs / step time)
+  fwd_tflops ...  the forward and backward alone, and both as % of the bf16 dense MFMA peak
+  roofline        the dominant kernel (largest share of step time), timed with HIP events
+                  on its own stream, against the MFMA peak
+  cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
+
+FLOP convention: forward 4*B*H*N^2*D, backward 10*B*H*N^2*D (five N x N x D products,
+including the recompute of S), halved when causal.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (fwd; fwd+bwd) and % of MI355X bf16 MFMA peak"
+PEAK_MFMA_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16/fp16 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD_KEYS = {
+    "fwd_bf16_n4096": ("fwd_bf16_n4096", 0),
+    "fwd_bf16_n8192": ("fwd_bf16_long", 0),
+    "fwd_bf16_n16384": ("fwd_bf16_long", 1),
+    "causal_long_bf16": ("causal_long_bf16", 0),
+}
+for _i, (_n, _d) in enumerate([(2048, 64), (2048, 128), (4096, 64), (4096, 128), (4000, 64), (4000, 128)]):
+    WORKLOAD_KEYS[f"gqa_causal_fp16_n{_n}_d{_d}"] = ("gqa_causal_fp16", _i)
+
+
+def flops(shape, fwd=True, bwd=True):
+    f = 4.0 * shape.B * shape.Hq * shape.N * shape.N * shape.D
+    if shape.causal:
+        f /= 2
+    return (f if fwd else 0.0) + (2.5 * f if bwd else 0.0)
+
+
+def cpu_baseline(shape, seed, budget_s):
+    """Time the float64 oracle's fwd+bwd on whole (batch, kv-group) units until ~budget_s."""
+    import numpy as np
+    from exact_attention_fa_amd.inputs import make_inputs
+    from oracle import attention_backward, attention_forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v, do = make_inputs(shape, seed)
+    grp = shape.Hq // shape.Hkv
+    f = lambda t: t.double().numpy()
+    units = [(b, kv) for b in range(shape.B) for kv in range(shape.Hkv)]
+    done, t0 = 0, time.perf_counter()
+    for b, kv in units:
+        hs = slice(kv * grp, (kv + 1) * grp)
+        qs, ks, vs, dos = f(q[b:b + 1, hs]), f(k[b:b + 1, kv:kv + 1]), f(v[b:b + 1, kv:kv + 1]), f(do[b:b + 1, hs])
+        attention_forward(qs, ks, vs, shape.scale, shape.causal)
+        attention_backward(qs, ks, vs, dos, shape.scale, shape.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    unit_flops = flops(shape) / len(units)
+    return {
+        "value": round(done * unit_flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} of {len(units)} (batch, kv-group) units of the workload, fwd+bwd in float64 "
+                   f"(NumPy, {threads} BLAS threads), {dt:.1f} s; the oracle computes the full N^2 work even "
+                   f"when causal, rated with the same algorithmic FLOP convention"),
+        "host_cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwd_bf16_n4096", choices=sorted(WORKLOAD_KEYS))
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (attention heads and "
+              "batches shard with no communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_fa_amd as fa
+    from exact_attention_fa_amd.inputs import WORKLOADS, make_inputs, workload_seed
+
+    name, variant = WORKLOAD_KEYS[args.workload]
+    shape = WORKLOADS[name][variant]
+    seed = workload_seed(name, variant)
+    fa.load_library()
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (t.to(dev) for t in make_inputs(shape, seed))
+    B, Hq, Hkv, N, D = shape.B, shape.Hq, shape.Hkv, shape.N, shape.D
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D), dtype=torch.uint8, device=dev)
+    causal, scale = shape.causal, shape.scale
+    stream = torch.cuda.current_stream(dev)
+
+    kernels = ["fwd", "bwd_preprocess", "bwd_main", "bwd_postprocess"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, causal=causal, softmax_scale=scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_bwd_preprocess(o, do, ws, Hkv)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_bwd_main(q, k, v, do, lse, dk, dv, ws, causal=causal, softmax_scale=scale)
+        if ev is not None:
+            ev[3].record(stream)
+        fa.fa_bwd_postprocess(dq, dk, dv, ws, Hkv, softmax_scale=scale)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, bracketed by device synchronisation.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel = {kname: [] for kname in kernels}
+    step_ms = []
+    for ev in evs:
+        for i, kname in enumerate(kernels):
+            per_kernel[kname].append(ev[i].elapsed_time(ev[i + 1]))
+        step_ms.append(ev[0].elapsed_time(ev[4]))
+    avg = {kname: statistics.fmean(vals) for kname, vals in per_kernel.items()}
+    med = {kname: statistics.median(vals) for kname, vals in per_kernel.items()}
+    ms_per_step = wall * 1e3 / args.steps
+
+    f_fwd, f_bwd = flops(shape, True, False), flops(shape, False, True)
+    fwd_ms = avg["fwd"]
+    bwd_ms = avg["bwd_preprocess"] + avg["bwd_main"] + avg["bwd_postprocess"]
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    dominant = max(kernels, key=lambda kname: avg[kname])
+    kflops = {"fwd": f_fwd, "bwd_main": f_bwd, "bwd_preprocess": 0.0, "bwd_postprocess": 0.0}
+    if kflops[dominant] > 0:
+        achieved = kflops[dominant] / (avg[dominant] * 1e-3) / 1e12
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                    "traffic": None, "avg_ms": round(avg[dominant], 4)}
+    else:  # pragma: no cover - the contractions dominate every listed workload
+        roofline = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D,
+                   "causal": causal, "softmax_scale": scale, "inputs": "N(0,1) seeded, cast RNE"
+                   + (f", x{shape.mult}" if shape.mult != 1.0 else "")},
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+        "fwd_pct_peak": round(100 * f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 2),
+        "fwd_bwd_pct_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "kernel_avg_ms": {kname: round(val, 4) for kname, val in avg.items()},
+        "kernel_median_ms": {kname: round(val, 4) for kname, val in med.items()},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, seed, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

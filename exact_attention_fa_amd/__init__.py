@@ -1,0 +1,209 @@
+"""Python binding of the MI355X fused exact-attention library (``libfa_mi355x.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in ``include/fa.h``.  PyTorch provides device memory and
+the current stream.  There is no fallback: if the library is missing or a call is
+rejected, a ``RuntimeError`` is raised.
+
+The functions carry the C entry points' names:
+
+    o, lse = fa_fwd(q, k, v, causal=False, softmax_scale=None)
+    dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=False, softmax_scale=None)
+
+q: (B, Hq, N, D), k and v: (B, Hkv, N, D), contiguous CUDA(HIP) tensors of dtype
+torch.float16 or torch.bfloat16, D in {64, 128}, Hq a multiple of Hkv.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = [
+    "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_postprocess",
+    "fa_bwd_workspace_size", "fa_version", "fa_status_string", "library_path", "load_library",
+    "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16",
+]
+
+FA_FP16 = 0
+FA_BF16 = 1
+_LIB_NAME = "libfa_mi355x.so"
+_lock = threading.Lock()
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGS = {
+    "fa_version": ([], ctypes.c_int),
+    "fa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "fa_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float,
+                ctypes.c_int, ctypes.c_int, _vp], ctypes.c_int),
+    "fa_bwd_workspace_size": ([_i64, _i64, _i64, _i64, _i64], ctypes.c_size_t),
+    "fa_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
+               ctypes.c_int),
+    "fa_bwd_preprocess": ([_vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
+                           ctypes.c_int, _vp], ctypes.c_int),
+    "fa_bwd_main": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                     _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
+                    ctypes.c_int),
+    "fa_bwd_postprocess": ([_vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
+                            ctypes.c_float, ctypes.c_int, _vp], ctypes.c_int),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+
+
+def load_library():
+    """Load (once) and return the ctypes handle; raises if the library is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build it with `python -m exact_attention_fa_amd._build` "
+                    "(or __graft_entry__.build()); there is no non-HIP fallback")
+            lib = ctypes.CDLL(path)
+            for name, (args, res) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = lib
+    return _lib
+
+
+def fa_version() -> int:
+    return load_library().fa_version()
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed: {fa_status_string(rc)} (status {rc})")
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return FA_FP16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise RuntimeError(f"unsupported dtype {t.dtype}: float16 or bfloat16 only")
+
+
+def _dims(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise RuntimeError("q, k, v must be 4-D (B, H, N, D)")
+    B, Hq, N, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
+        raise RuntimeError("k and v must be (B, Hkv, N, D) with the B, N, D of q")
+    return B, Hq, k.shape[1], N, D
+
+
+def _require(*tensors, dtype=None):
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise RuntimeError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise RuntimeError("tensors must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise RuntimeError(f"dtype mismatch: expected {dtype}, got {t.dtype}")
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _scale(D, softmax_scale):
+    return 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+
+
+def fa_fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
+    """Forward: returns (o, lse); o like q, lse float32 (B, Hq, N) in natural-log units."""
+    import torch
+    B, Hq, Hkv, N, D = _dims(q, k, v)
+    _require(q, k, v, dtype=q.dtype)
+    code = _dtype_code(q)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o, dtype=q.dtype)
+    _require(l, dtype=torch.float32)
+    rc = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, Hq, Hkv, N, D,
+                               _scale(D, softmax_scale), int(bool(causal)), code, _stream(q))
+    _check(rc, "fa_fwd")
+    return o, l
+
+
+def fa_bwd_workspace_size(B, Hq, Hkv, N, D) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, Hq, Hkv, N, D))
+
+
+def _workspace(q, shape, workspace):
+    import torch
+    need = fa_bwd_workspace_size(*shape)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def fa_bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale=None, workspace=None,
+           dq=None, dk=None, dv=None):
+    """Backward: returns (dq, dk, dv) in the dtype of q."""
+    import torch
+    B, Hq, Hkv, N, D = _dims(q, k, v)
+    _require(q, k, v, o, do, dtype=q.dtype)
+    _require(lse, dtype=torch.float32)
+    code = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, dk, dv, dtype=q.dtype)
+    ws, nbytes = _workspace(q, (B, Hq, Hkv, N, D), workspace)
+    rc = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(ws), nbytes, B, Hq, Hkv, N, D,
+                               _scale(D, softmax_scale), int(bool(causal)), code, _stream(q))
+    _check(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_preprocess(o, do, workspace, Hkv: int):
+    B, Hq, N, D = o.shape
+    _require(o, do, dtype=o.dtype)
+    rc = load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          B, Hq, Hkv, N, D, _dtype_code(o), _stream(o))
+    _check(rc, "fa_bwd_preprocess")
+
+
+def fa_bwd_main(q, k, v, do, lse, dk, dv, workspace, causal=False, softmax_scale=None):
+    B, Hq, Hkv, N, D = _dims(q, k, v)
+    rc = load_library().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk),
+                                    _ptr(dv), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, D,
+                                    _scale(D, softmax_scale), int(bool(causal)), _dtype_code(q),
+                                    _stream(q))
+    _check(rc, "fa_bwd_main")
+
+
+def fa_bwd_postprocess(dq, dk, dv, workspace, Hkv: int, softmax_scale=None):
+    B, Hq, N, D = dq.shape
+    rc = load_library().fa_bwd_postprocess(_ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           B, Hq, Hkv, N, D, _scale(D, softmax_scale),
+                                           _dtype_code(dq), _stream(dq))
+    _check(rc, "fa_bwd_postprocess")

@@ -1,0 +1,238 @@
+// C-ABI entry points: argument validation, workspace layout and dispatch to the HIP
+// launchers.  Every check happens before anything is enqueued, so a rejected call has no
+// side effect ("FlashAttention for Tesla P100", section "What it supports": unsupported
+// requests raise instead of degrading quietly).
+#include "../../include/fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+size_t round_up(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+int check_dims(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return FA_ERR_BAD_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  const int64_t lim = INT32_MAX;
+  // The kernels index heads, rows and grid blocks with 32-bit integers.
+  if (N > lim / D || B > lim / Hq || B * Hq > lim / N) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+int check_dtype(int dtype) { return (dtype == FA_FP16 || dtype == FA_BF16) ? FA_OK : FA_ERR_DTYPE; }
+
+int check_scale(float s) { return (isfinite(s) && s >= 0.f) ? FA_OK : FA_ERR_SCALE; }
+
+int check_ptr(const void* p, uintptr_t align) {
+  if (p == nullptr) return FA_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(p) % align != 0) return FA_ERR_ALIGNMENT;
+  return FA_OK;
+}
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  bool output;
+};
+
+// Outputs may not overlap any other buffer of the call.
+int check_alias(const Range* r, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!r[i].output || r[i].p == nullptr) continue;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(r[i].p), a1 = a0 + r[i].bytes;
+    for (int j = 0; j < n; ++j) {
+      if (j == i || r[j].p == nullptr) continue;
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(r[j].p), b1 = b0 + r[j].bytes;
+      if (a0 < b1 && b0 < a1) return FA_ERR_ALIAS;
+    }
+  }
+  return FA_OK;
+}
+
+#define FA_TRY(expr)              \
+  do {                            \
+    const int _rc = (expr);       \
+    if (_rc != FA_OK) return _rc; \
+  } while (0)
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long long N, long long D) {
+  BwdWorkspace w{};
+  const size_t rows = (size_t)B * (size_t)Hq * (size_t)N;
+  size_t off = 0;
+  w.dq_acc = off;
+  off += round_up(rows * (size_t)D * 4);
+  w.delta = off;
+  off += round_up(rows * 4);
+  if (Hq != Hkv) {
+    w.dk_part = off;
+    off += round_up(rows * (size_t)D * 4);
+    w.dv_part = off;
+    off += round_up(rows * (size_t)D * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "B, Hq, Hkv and N must be positive";
+    case FA_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
+    case FA_ERR_GQA: return "Hq must be a multiple of Hkv";
+    case FA_ERR_DTYPE: return "dtype must be FA_FP16 or FA_BF16";
+    case FA_ERR_SCALE: return "softmax_scale must be finite and >= 0";
+    case FA_ERR_ALIGNMENT: return "buffers must be 16-byte aligned (lse: 4-byte)";
+    case FA_ERR_WORKSPACE: return "workspace is smaller than fa_bwd_workspace_size()";
+    case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_TOO_LARGE: return "problem size exceeds the 32-bit index range of the kernels";
+    case FA_ERR_ALIAS: return "an output buffer overlaps another buffer of the call";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+           int64_t Hkv, int64_t N, int64_t D, float softmax_scale, int causal, int dtype, void* stream) {
+  FA_TRY(check_dtype(dtype));
+  FA_TRY(check_dims(B, Hq, Hkv, N, D));
+  FA_TRY(check_scale(softmax_scale));
+  FA_TRY(check_ptr(q, 16));
+  FA_TRY(check_ptr(k, 16));
+  FA_TRY(check_ptr(v, 16));
+  FA_TRY(check_ptr(o, 16));
+  FA_TRY(check_ptr(lse, 4));
+  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {o, qb, true},
+                     {lse, (size_t)(B * Hq * N) * 4, true}};
+  FA_TRY(check_alias(r, 5));
+  FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, D, softmax_scale, causal != 0, dtype == FA_BF16,
+            static_cast<hipStream_t>(stream)};
+  return status_of(launch_fwd(a));
+}
+
+size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D) {
+  if (check_dims(B, Hq, Hkv, N, D) != FA_OK) return 0;
+  return bwd_workspace_layout(B, Hq, Hkv, N, D).total;
+}
+
+namespace {
+
+// Validation common to the backward entry points; pointers are checked by the callers.
+int check_bwd_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
+                     const void* ws, size_t ws_bytes) {
+  FA_TRY(check_dtype(dtype));
+  FA_TRY(check_dims(B, Hq, Hkv, N, D));
+  FA_TRY(check_ptr(ws, 16));
+  if (ws_bytes < bwd_workspace_layout(B, Hq, Hkv, N, D).total) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, void* ws, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t N, int64_t D, float scale, int causal, int dtype, void* stream) {
+  return BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, static_cast<char*>(ws), B, Hq, Hkv, N, D, scale,
+                 causal != 0, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
+}
+
+}  // namespace
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
+           int64_t Hkv, int64_t N, int64_t D, float softmax_scale, int causal, int dtype, void* stream) {
+  FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
+  FA_TRY(check_scale(softmax_scale));
+  const void* p16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : p16) FA_TRY(check_ptr(p, 16));
+  FA_TRY(check_ptr(lse, 4));
+  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const Range r[] = {{q, qb, false},  {k, kb, false},  {v, kb, false},  {o, qb, false},
+                     {dout, qb, false}, {lse, (size_t)(B * Hq * N) * 4, false},
+                     {dq, qb, true},  {dk, kb, true},  {dv, kb, true},
+                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, true}};
+  FA_TRY(check_alias(r, 10));
+  const BwdArgs a = make_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, D, softmax_scale,
+                                  causal, dtype, stream);
+  FA_TRY(status_of(launch_bwd_preprocess(a)));
+  FA_TRY(status_of(launch_bwd_main(a)));
+  return status_of(launch_bwd_postprocess(a));
+}
+
+int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int64_t B,
+                      int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype, void* stream) {
+  FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
+  FA_TRY(check_ptr(o, 16));
+  FA_TRY(check_ptr(dout, 16));
+  const size_t qb = (size_t)(B * Hq * N * D) * 2;
+  const Range r[] = {{o, qb, false}, {dout, qb, false},
+                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, true}};
+  FA_TRY(check_alias(r, 3));
+  const BwdArgs a = make_bwd_args(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, workspace,
+                                  B, Hq, Hkv, N, D, 1.f, 0, dtype, stream);
+  return status_of(launch_bwd_preprocess(a));
+}
+
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                float softmax_scale, int causal, int dtype, void* stream) {
+  FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
+  FA_TRY(check_scale(softmax_scale));
+  const void* p16[] = {q, k, v, dout};
+  for (const void* p : p16) FA_TRY(check_ptr(p, 16));
+  FA_TRY(check_ptr(lse, 4));
+  const bool direct = Hq == Hkv;
+  if (direct) {
+    FA_TRY(check_ptr(dk, 16));
+    FA_TRY(check_ptr(dv, 16));
+  }
+  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {dout, qb, false},
+                     {lse, (size_t)(B * Hq * N) * 4, false},
+                     {direct ? dk : nullptr, kb, true}, {direct ? dv : nullptr, kb, true},
+                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, true}};
+  FA_TRY(check_alias(r, 8));
+  const BwdArgs a = make_bwd_args(q, k, v, nullptr, dout, lse, nullptr, dk, dv, workspace, B, Hq, Hkv, N, D,
+                                  softmax_scale, causal, dtype, stream);
+  return status_of(launch_bwd_main(a));
+}
+
+int fa_bwd_postprocess(void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B,
+                       int64_t Hq, int64_t Hkv, int64_t N, int64_t D, float softmax_scale, int dtype,
+                       void* stream) {
+  FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
+  FA_TRY(check_scale(softmax_scale));
+  FA_TRY(check_ptr(dq, 16));
+  const bool reduce = Hq != Hkv;
+  if (reduce) {
+    FA_TRY(check_ptr(dk, 16));
+    FA_TRY(check_ptr(dv, 16));
+  }
+  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const Range r[] = {{dq, qb, true}, {reduce ? dk : nullptr, kb, true}, {reduce ? dv : nullptr, kb, true},
+                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, false}};
+  FA_TRY(check_alias(r, 4));
+  const BwdArgs a = make_bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, workspace, B,
+                                  Hq, Hkv, N, D, softmax_scale, 0, dtype, stream);
+  return status_of(launch_bwd_postprocess(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+// Fused exact attention forward for gfx950.
+//
+// The method ("From-scratch CUDA attention kernel reaches 94.4% of FlashAttention-4 on
+// NVIDIA B200", section "How the kernel partitions its work"): one workgroup owns one
+// tile of query rows, keeps it on chip, and streams the K/V tiles of its head past it;
+// per K/V tile it forms the scores, updates a running row maximum and running row sum
+// (the online softmax of "FlashStieltjes", section "The challenge"), rescales and adds
+// P V into a private accumulator, and normalises once at the end.  The N x N score
+// matrix never exists in memory.  Causal attention visits only the K/V tiles on or
+// below the diagonal ("FlashAttention for Tesla P100", section "What it supports").
+//
+// gfx950 realisation:
+//   * 256 threads = 4 waves; a wave owns 32 query rows (BR = 128 rows per workgroup).
+//   * K/V tiles of BC = 64 keys staged through LDS (swizzled row-major), prefetched into
+//     registers one tile ahead so global latency overlaps the MFMA/softmax work.
+//   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16: each lane then
+//     owns one query column, its row max and row sum are in-lane reductions plus one
+//     v_permlane32_swap, and the bf16/fp16-rounded probabilities in registers are already
+//     the B operand of O^T += V^T P^T.  V^T comes from the row-major V tile through
+//     ds_read_b64_tr_b16.
+//   * exp2 on the VALU with scale*log2(e) folded into one FMA per score.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kFwdBR = 128;  // query rows per workgroup
+constexpr int kFwdBC = 64;   // keys per K/V tile
+constexpr int kThreads = 256;
+
+template <typename TR, int HD, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads, 2)
+fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+           const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+           int Hq, int Hkv, int N, int n_qt, float c2, float scale) {
+  constexpr int BR = kFwdBR, BC = kFwdBC;
+  constexpr int KST = HD / 16;                 // k-steps of S^T over the head dim
+  constexpr int DB = HD / 32;                  // 32-row blocks of O^T
+  constexpr int TILE = BC * HD * 2;            // bytes of one K or V tile
+  constexpr int CPR = HD / 8;                  // 16-byte chunks per row
+  constexpr int CH = BC * CPR / kThreads;      // chunks per thread per tile
+  static_assert(CH * kThreads == BC * CPR, "tile must split evenly over the workgroup");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE];
+  char* const sK = smem;
+  char* const sV = smem + TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, g = lane >> 5;
+
+  const int job = xcd_remap(blockIdx.x, gridDim.x);
+  int qt = job % n_qt;
+  const int bh = job / n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  const int hq = bh % Hq, b = bh / Hq;
+  const int hkv = hq / (Hq / Hkv);
+  const uint16_t* const Qh = Q + (size_t)bh * N * HD;
+  const uint16_t* const Kh = K + ((size_t)b * Hkv + hkv) * N * HD;
+  const uint16_t* const Vh = V + ((size_t)b * Hkv + hkv) * N * HD;
+
+  const int qw0 = qt * BR + wave * 32;  // first query row of this wave
+  const int qi = qw0 + c;               // the query row this lane's column belongs to
+
+  // Q fragments: B operand of S^T = K Q^T (slot j of k-step kk = Q[qi][kk*16 + g*8 + j]).
+  u32x4 qf[KST];
+#pragma unroll
+  for (int kk = 0; kk < KST; ++kk) qf[kk] = ld16_if(Qh + (size_t)qi * HD + kk * 16 + g * 8, qi < N);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY;  // running max of raw scores for query qi
+  float l_run = 0.f;        // this lane's share of the running sum of 2^((s - m) * c2)
+
+  int kv_end = (N + BC - 1) / BC;
+  if (CAUSAL) kv_end = (min(N, (qt + 1) * BR) - 1) / BC + 1;
+
+  u32x4 kreg[CH], vreg[CH];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      const int cid = tid + kThreads * r;
+      const int row = cid / CPR, ch = cid % CPR;
+      const int key = t * BC + row;
+      kreg[r] = ld16_if(Kh + (size_t)key * HD + ch * 8, key < N);
+      vreg[r] = ld16_if(Vh + (size_t)key * HD + ch * 8, key < N);
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      const int cid = tid + kThreads * r;
+      const int row = cid / CPR, ch = cid % CPR;
+      lds_write8<HD>(sK, row, ch * 8, kreg[r]);
+      lds_write8<HD>(sV, row, ch * 8, vreg[r]);
+    }
+  };
+
+  gload(0);
+  for (int t = 0; t < kv_end; ++t) {
+    __syncthreads();  // every wave is done reading the previous tile
+    lstore();
+    __syncthreads();
+    if (t + 1 < kv_end) gload(t + 1);
+
+    const int kv0 = t * BC;
+    if (CAUSAL && kv0 > qw0 + 31) continue;  // tile lies above the diagonal for this wave
+
+    // ---- S^T = K Q^T: register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) {
+        const u32x4 a = lds_read8<HD>(sK, kb * 32 + perm_rows(c), kk * 16 + g * 8);
+        s[kb] = TR::mfma(a, qf[kk], s[kb]);
+      }
+    }
+
+    // ---- masks (ragged tail, causal diagonal): only on tiles that need them
+    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+    uint32_t dead = 0;
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          const bool off = key >= N || (CAUSAL && key > qi);
+          if (off) {
+            dead |= 1u << (kb * 16 + i);
+            s[kb][i] = -INFINITY;
+          }
+        }
+    }
+
+    // ---- online softmax (scores in raw units; c2 = scale * log2(e) >= 0)
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m_run, mx);  // finite: key 0 of tile 0 is visible to every row
+    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c2);
+    const float mb = m_new * c2;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[kb][i], c2, -mb));
+        if (need_mask && ((dead >> (kb * 16 + i)) & 1u)) p = 0.f;
+        s[kb][i] = p;
+        rs += p;
+      }
+    l_run = fmaf(l_run, alpha, rs);
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+
+    // ---- P^T operands: slot j of (kb, t2) = P for key kv0 + kb*32 + t2*16 + g*8 + j
+    u32x4 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int i0 = t2 * 8;
+        pb[kb][t2] = u32x4{TR::pack(s[kb][i0 + 0], s[kb][i0 + 1]), TR::pack(s[kb][i0 + 2], s[kb][i0 + 3]),
+                           TR::pack(s[kb][i0 + 4], s[kb][i0 + 5]), TR::pack(s[kb][i0 + 6], s[kb][i0 + 7])};
+      }
+
+    // ---- O^T += V^T P^T  (A = V^T rows d, k = keys, read transposed from the V tile)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 a = lds_read_tr8<HD>(sV, kb * 32 + t2 * 16, db * 32, lane);
+          acc[db] = TR::mfma(a, pb[kb][t2], acc[db]);
+        }
+  }
+
+  // ---- epilogue: normalise, write O (input dtype, RNE) and LSE (natural log, fp32)
+  const float l_tot = pair_sum(l_run);
+  const float inv = 1.f / l_tot;
+  if (qi < N) {
+    uint16_t* const orow = O + (size_t)bh * N * HD + (size_t)qi * HD;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = db * 32 + i4 * 8 + g * 4;
+        const u32x2 w = {TR::pack(acc[db][i4 * 4 + 0] * inv, acc[db][i4 * 4 + 1] * inv),
+                         TR::pack(acc[db][i4 * 4 + 2] * inv, acc[db][i4 * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d) = w;
+      }
+    if (g == 0) LSE[(size_t)bh * N + qi] = m_run * scale + __logf(l_tot);
+  }
+}
+
+template <typename TR, int HD, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdArgs& a) {
+  const int n_qt = (int)((a.N + kFwdBR - 1) / kFwdBR);
+  const long long blocks = a.B * a.Hq * (long long)n_qt;
+  const float c2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale);
+  return hipGetLastError();
+}
+
+template <typename TR>
+hipError_t launch_fwd_dt(const FwdArgs& a) {
+  if (a.D == 64) return a.causal ? launch_fwd_t<TR, 64, true>(a) : launch_fwd_t<TR, 64, false>(a);
+  return a.causal ? launch_fwd_t<TR, 128, true>(a) : launch_fwd_t<TR, 128, false>(a);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  return a.bf16 ? launch_fwd_dt<Bf16>(a) : launch_fwd_dt<F16>(a);
+}
+
+}  // namespace fa

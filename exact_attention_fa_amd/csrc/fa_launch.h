@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI layer (fa_api.cpp) and the kernel launchers.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  long long B, Hq, Hkv, N, D;
+  float scale;
+  bool causal;
+  bool bf16;
+  hipStream_t stream;
+};
+
+// Workspace carve-up used by the backward stages (byte offsets from the base).
+struct BwdWorkspace {
+  size_t dq_acc;   // fp32 (B, Hq, N, D): dQ accumulated over K/V tiles
+  size_t delta;    // fp32 (B, Hq, N): D = rowsum(dO * O)
+  size_t dk_part;  // fp32 (B, Hq, N, D): per-query-head dK partials (only when Hq > Hkv)
+  size_t dv_part;  // fp32 (B, Hq, N, D): per-query-head dV partials (only when Hq > Hkv)
+  size_t total;
+};
+BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long long N, long long D);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  char* ws;
+  long long B, Hq, Hkv, N, D;
+  float scale;
+  bool causal;
+  bool bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd_preprocess(const BwdArgs& a);
+hipError_t launch_bwd_main(const BwdArgs& a);
+hipError_t launch_bwd_postprocess(const BwdArgs& a);
+
+}  // namespace fa

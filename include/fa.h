@@ -1,0 +1,138 @@
+/*
+ * fa.h - C ABI of a fused, tiled, exact scaled-dot-product attention library for
+ * AMD MI355X (gfx950).
+ *
+ * The operation ("From-scratch CUDA attention kernel reaches 94.4% of FlashAttention-4
+ * on NVIDIA B200", section "How the kernel partitions its work"; "FlashAttention for
+ * Tesla P100", sections "What it supports" and "Documentation"):
+ *
+ *   S   = scale * Q K^T                         per (batch, query head)
+ *   P   = softmax over the visible keys of each row of S
+ *   O   = P V
+ *   LSE = log-sum-exp (natural log) of each row of S over its visible keys
+ *
+ * and its gradient for an upstream dO, with D = rowsum(dO * O):
+ *
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q
+ *
+ * where P is recomputed from the saved LSE.  The N x N matrices S and P are never
+ * stored.
+ *
+ * Conventions shared by every entry point
+ *   Layout     Q, O, dO, dQ: (B, Hq, N, D); K, V, dK, dV: (B, Hkv, N, D); LSE: (B, Hq, N).
+ *              All contiguous row-major, D innermost, no strides.  Sequence length N is
+ *              the same for queries and keys (self-attention).
+ *   dtype      FA_FP16 or FA_BF16 for every 16-bit tensor of a call; LSE, the backward
+ *              workspace and all accumulation are fp32.  Outputs are rounded to nearest
+ *              even.
+ *   Heads      Hq must be a multiple of Hkv; query head h reads KV head h / (Hq / Hkv)
+ *              (MHA, GQA and MQA).
+ *   Causal     causal != 0: key j is visible to query i iff j <= i (square, top-left).
+ *              Blocks above the diagonal are skipped, not computed and masked.
+ *   Scale      softmax_scale must be finite and >= 0 (0 gives uniform attention).
+ *   D          64 or 128.  N >= 1, arbitrary (ragged tails need no padding).
+ *   Pointers   device pointers, 16-byte aligned, not aliasing one another.  The caller
+ *              owns every buffer; inputs are only read, outputs are fully overwritten.
+ *   Stream     a hipStream_t passed as void*; NULL is the default stream.  Work is only
+ *              enqueued: nothing synchronises, allocates or frees device memory, and the
+ *              library keeps no mutable global state.
+ *   Errors     every argument is checked before anything is enqueued; on a non-zero
+ *              status nothing was launched and no output was touched.  FA_ERR_HIP means a
+ *              launch was rejected by the runtime.  Faults inside a kernel surface at the
+ *              caller's next synchronisation, as for any stream library.
+ *   Not offered (rejected by construction rather than silently degraded): dropout,
+ *              attention bias, arbitrary or padding masks, sliding windows, block
+ *              sparsity, KV-cache decoding, Nq != Nk, other head dims.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype {
+  FA_FP16 = 0,
+  FA_BF16 = 1
+};
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,    /* B, Hq, Hkv or N <= 0 */
+  FA_ERR_HEAD_DIM = 3,     /* D is not 64 or 128 */
+  FA_ERR_GQA = 4,          /* Hq is not a multiple of Hkv */
+  FA_ERR_DTYPE = 5,        /* dtype is not FA_FP16 / FA_BF16 */
+  FA_ERR_SCALE = 6,        /* softmax_scale is negative, NaN or infinite */
+  FA_ERR_ALIGNMENT = 7,    /* a pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 8,    /* workspace_bytes < fa_bwd_workspace_size(...) */
+  FA_ERR_HIP = 9,          /* the HIP runtime rejected a launch */
+  FA_ERR_TOO_LARGE = 10,   /* a size exceeds the 32-bit index range the kernels use */
+  FA_ERR_ALIAS = 11        /* an output buffer overlaps another buffer of the call */
+};
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * Forward.  Reads q (B,Hq,N,D), k and v (B,Hkv,N,D); writes o (B,Hq,N,D, same dtype)
+ * and lse (B,Hq,N, fp32, natural-log units of the scaled scores).  One kernel launch.
+ * Bitwise deterministic.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+           float softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs (fp32 dQ accumulator, the D vector and, when
+ * Hq > Hkv, per-query-head dK/dV partials).  Returns 0 for invalid shapes.
+ */
+size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D);
+
+/*
+ * Backward.  Inputs q, k, v, o (from fa_fwd), dout (dO, shape of q), lse (from fa_fwd);
+ * outputs dq (shape of q), dk and dv (shape of k); all 16-bit tensors in `dtype`.
+ * workspace: caller-owned device memory of at least fa_bwd_workspace_size(...) bytes,
+ * contents undefined before and after.  Enqueues, in order, fa_bwd_preprocess,
+ * fa_bwd_main and fa_bwd_postprocess.  dK and dV are deterministic; dQ is accumulated
+ * with fp32 atomics, so its last bits may vary from run to run.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+           int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+           float softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * The three stages of fa_bwd, exported so a caller (or a profiler harness) can place
+ * events between them.  Running them in this order on one stream with the same
+ * workspace is exactly fa_bwd.
+ *   fa_bwd_preprocess:  workspace.D = rowsum(dout * o) in fp32; zeroes the dQ accumulator.
+ *   fa_bwd_main:        recomputes P, adds scale-free dS K into the dQ accumulator, and
+ *                       writes dk/dv (Hq == Hkv) or fp32 per-query-head partials into the
+ *                       workspace (Hq > Hkv).  Needs the preprocess results.
+ *   fa_bwd_postprocess: dq = scale * accumulator in `dtype`; for Hq > Hkv also sums the
+ *                       dK/dV partials over each group into dk/dv.
+ * Arguments a stage does not use may be NULL (and are then not checked).
+ */
+int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
+                      void* stream);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                float softmax_scale, int causal, int dtype, void* stream);
+int fa_bwd_postprocess(void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                       float softmax_scale, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

@@ -1,0 +1,115 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI, run the
+oracle on the same seeded inputs, compare with the stated tolerances.
+
+Tolerances (float; inputs bf16/fp16, fp32 accumulation):
+  O    max |O_gpu - O_ref|                    <= 1e-2
+  LSE  max |LSE_gpu - LSE_ref|                <= 1e-3
+  dQ, dK, dV  max |g - g_ref| / max(max |g_ref|, 1e-2)   <= 2e-2   (per tensor)
+The 1e-2 floor only matters when the exact gradient vanishes (e.g. N = 1, where
+dS = P (dP - D) = 0): the check then becomes an absolute bound of 2e-4.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import exact_attention_fa_amd as fa
+from exact_attention_fa_amd.inputs import Shape, make_inputs
+from oracle import attention_backward, attention_forward
+
+TOL_O = 1e-2
+TOL_LSE = 1e-3
+TOL_GRAD = 2e-2
+GRAD_FLOOR = 1e-2
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def gpu_forward(q, k, v, causal, scale):
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def gpu_backward(q, k, v, o, do, lse, causal, scale):
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, dod, lse, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def rel_err(g, ref):
+    return float(np.abs(g - ref).max() / max(np.abs(ref).max(), GRAD_FLOOR))
+
+
+def assert_fwd_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
+    eo = float(np.abs(o_gpu - o_ref).max())
+    el = float(np.abs(lse_gpu - lse_ref).max())
+    assert np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all(), what
+    assert eo <= TOL_O, f"{what}: O max-abs error {eo:.3e} > {TOL_O}"
+    assert el <= TOL_LSE, f"{what}: LSE max-abs error {el:.3e} > {TOL_LSE}"
+    return eo, el
+
+
+def assert_grad_close(g, ref, name, what=""):
+    assert np.isfinite(g).all(), f"{what}: {name} has non-finite values"
+    e = rel_err(g, ref)
+    assert e <= TOL_GRAD, f"{what}: {name} relative max error {e:.3e} > {TOL_GRAD}"
+    return e
+
+
+def full_check(shape: Shape, seed: int, backward: bool = True, scale=None):
+    """Element-by-element comparison of every output against the oracle."""
+    scale = shape.scale if scale is None else scale
+    q, k, v, do = make_inputs(shape, seed)
+    o, lse = gpu_forward(q, k, v, shape.causal, scale)
+    o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v), scale, shape.causal)
+    errs = dict(zip(("o", "lse"), assert_fwd_close(f64(o), f64(lse), o_ref, lse_ref, str(shape))))
+    if backward:
+        dq, dk, dv = gpu_backward(q, k, v, o, do, lse, shape.causal, scale)
+        dq_r, dk_r, dv_r = attention_backward(f64(q), f64(k), f64(v), f64(do), scale, shape.causal)
+        for name, g, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
+            errs[name] = assert_grad_close(f64(g), r, name, str(shape))
+    return errs
+
+
+def sampled_check(shape: Shape, seed: int, units, n_rows: int, backward: bool, rng_seed: int = 0):
+    """Full-size GPU run; the oracle recomputes sampled outputs of some (batch, kv-group) units.
+
+    ``units`` lists (b, kv) pairs; each unit is the sub-problem of KV head kv of batch b and
+    its Hq/Hkv query heads, which the oracle solves exactly (heads are independent).  Within
+    a unit, ``n_rows`` query rows (for O, LSE, dQ) and ``n_rows`` keys (for dK, dV) are
+    compared, always including the first and last index and the start of the last tile.
+    """
+    q, k, v, do = make_inputs(shape, seed, with_grad=backward)
+    o, lse = gpu_forward(q, k, v, shape.causal, shape.scale)
+    grads = gpu_backward(q, k, v, o, do, lse, shape.causal, shape.scale) if backward else None
+    o_h, lse_h = f64(o), f64(lse)
+    if backward:
+        dq_h, dk_h, dv_h = (f64(t) for t in grads)
+    rng = np.random.default_rng(rng_seed)
+    N, grp = shape.N, shape.Hq // shape.Hkv
+    errs = {"o": 0.0, "lse": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b, kv in units:
+        hs = slice(kv * grp, (kv + 1) * grp)
+        must = [0, N - 1, max(0, (N - 1) // 64 * 64), N // 2]
+        idx = np.unique(np.concatenate([must, rng.choice(N, size=min(n_rows, N), replace=False)]))
+        qs, ks, vs = f64(q[b:b + 1, hs]), f64(k[b:b + 1, kv:kv + 1]), f64(v[b:b + 1, kv:kv + 1])
+        o_ref, lse_ref = attention_forward(qs, ks, vs, shape.scale, shape.causal, rows=idx)
+        eo, el = assert_fwd_close(o_h[b:b + 1, hs][:, :, idx], lse_h[b:b + 1, hs][:, :, idx], o_ref, lse_ref,
+                                  f"{shape} unit {(b, kv)}")
+        errs["o"], errs["lse"] = max(errs["o"], eo), max(errs["lse"], el)
+        if backward:
+            dos = f64(do[b:b + 1, hs])
+            dq_r, dk_r, dv_r = attention_backward(qs, ks, vs, dos, shape.scale, shape.causal, rows=idx, keys=idx)
+            # relative errors are normalised by the largest reference value of the sample
+            for name, g, r in (("dq", dq_h[b:b + 1, hs][:, :, idx], dq_r),
+                               ("dk", dk_h[b:b + 1, kv:kv + 1][:, :, idx], dk_r),
+                               ("dv", dv_h[b:b + 1, kv:kv + 1][:, :, idx], dv_r)):
+                errs[name] = max(errs[name], assert_grad_close(g, r, name, f"{shape} unit {(b, kv)}"))
+    return errs, (o, lse, grads)

@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/fa.h declares,
+and rejects invalid calls with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_fa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+STATUS = {
+    "FA_OK": 0, "FA_ERR_NULL_POINTER": 1, "FA_ERR_BAD_SHAPE": 2, "FA_ERR_HEAD_DIM": 3,
+    "FA_ERR_GQA": 4, "FA_ERR_DTYPE": 5, "FA_ERR_SCALE": 6, "FA_ERR_ALIGNMENT": 7,
+    "FA_ERR_WORKSPACE": 8, "FA_ERR_HIP": 9, "FA_ERR_TOO_LARGE": 10, "FA_ERR_ALIAS": 11,
+}
+
+# Fake, aligned, non-null "device" addresses: every call below fails validation before any
+# HIP call, so they are never dereferenced.
+A = 1 << 32
+MB = 1 << 20
+
+
+def ptr(i):
+    return ctypes.c_void_p(A + i * 64 * 1024 * MB)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        pytest.fail("libfa_mi355x.so is not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(fa_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTED_SYMBOLS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {fa.library_path()}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_header_status_values_match():
+    text = open(HEADER).read()
+    for name, val in STATUS.items():
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
+
+
+def test_version_and_strings(lib):
+    assert fa.fa_version() == 10000
+    for code in range(12):
+        s = fa.fa_status_string(code)
+        assert s and s != "unknown status"
+    assert fa.fa_status_string(999) == "unknown status"
+
+
+def fwd(lib, q=0, k=1, v=2, o=3, l=4, B=1, Hq=2, Hkv=2, N=256, D=64, scale=0.125, causal=0, dtype=0):
+    P = lambda x: x if isinstance(x, ctypes.c_void_p) else ptr(x)
+    return lib.fa_fwd(P(q), P(k), P(v), P(o), P(l), B, Hq, Hkv, N, D, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), "FA_ERR_DTYPE"),
+    (dict(dtype=-1), "FA_ERR_DTYPE"),
+    (dict(B=0), "FA_ERR_BAD_SHAPE"),
+    (dict(Hq=0), "FA_ERR_BAD_SHAPE"),
+    (dict(Hkv=-1), "FA_ERR_BAD_SHAPE"),
+    (dict(N=0), "FA_ERR_BAD_SHAPE"),
+    (dict(D=32), "FA_ERR_HEAD_DIM"),
+    (dict(D=96), "FA_ERR_HEAD_DIM"),
+    (dict(D=256), "FA_ERR_HEAD_DIM"),
+    (dict(Hq=6, Hkv=4), "FA_ERR_GQA"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(scale=float("inf")), "FA_ERR_SCALE"),
+    (dict(scale=-0.5), "FA_ERR_SCALE"),
+    (dict(N=1 << 26, D=128), "FA_ERR_TOO_LARGE"),
+    (dict(B=1 << 20, Hq=1 << 12, Hkv=1 << 12), "FA_ERR_TOO_LARGE"),
+    (dict(q=ctypes.c_void_p(0)), "FA_ERR_NULL_POINTER"),
+    (dict(l=ctypes.c_void_p(0)), "FA_ERR_NULL_POINTER"),
+    (dict(k=ctypes.c_void_p(A + 8)), "FA_ERR_ALIGNMENT"),
+    (dict(l=ctypes.c_void_p(A + 2)), "FA_ERR_ALIGNMENT"),
+    (dict(o=0), "FA_ERR_ALIAS"),
+    (dict(l=ctypes.c_void_p(A + 1024)), "FA_ERR_ALIAS"),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == STATUS[status]
+
+
+def test_workspace_size(lib):
+    B, Hq, Hkv, N, D = 1, 16, 4, 4000, 128
+    up = lambda x: (x + 255) // 256 * 256
+    rows = B * Hq * N
+    mha = up(rows * D * 4) + up(rows * 4)
+    assert fa.fa_bwd_workspace_size(B, Hq, Hq, N, D) == mha
+    assert fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D) == mha + 2 * up(rows * D * 4)
+    assert fa.fa_bwd_workspace_size(0, Hq, Hkv, N, D) == 0
+    assert fa.fa_bwd_workspace_size(B, Hq, Hkv, N, 96) == 0
+
+
+def bwd(lib, ws_bytes=None, B=1, Hq=2, Hkv=2, N=256, D=64, scale=0.125, dtype=0, **over):
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"]
+    ptrs = {n: ptr(i) for i, n in enumerate(names)}
+    ptrs.update(over)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D)
+    return lib.fa_bwd(*[ptrs[n] for n in names], ws_bytes, B, Hq, Hkv, N, D, scale, 0, dtype, None)
+
+
+def test_bwd_rejects(lib):
+    need = fa.fa_bwd_workspace_size(1, 2, 2, 256, 64)
+    assert bwd(lib, ws_bytes=need - 1) == STATUS["FA_ERR_WORKSPACE"]
+    assert bwd(lib, D=80) == STATUS["FA_ERR_HEAD_DIM"]
+    assert bwd(lib, dtype=7) == STATUS["FA_ERR_DTYPE"]
+    assert bwd(lib, scale=-1.0) == STATUS["FA_ERR_SCALE"]
+    assert bwd(lib, dq=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]
+    assert bwd(lib, dv=ctypes.c_void_p(A + 4)) == STATUS["FA_ERR_ALIGNMENT"]
+    assert bwd(lib, dq=ptr(0)) == STATUS["FA_ERR_ALIAS"]
+    assert bwd(lib, ws=ptr(1)) == STATUS["FA_ERR_ALIAS"]
+    assert bwd(lib, Hq=3, Hkv=2) == STATUS["FA_ERR_GQA"]
+
+
+def test_stage_entry_points_reject(lib):
+    B, Hq, Hkv, N, D = 1, 4, 2, 100, 128
+    need = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D)
+    assert lib.fa_bwd_preprocess(ptr(0), ptr(1), ptr(2), need - 16, B, Hq, Hkv, N, D, 1, None) == \
+        STATUS["FA_ERR_WORKSPACE"]
+    assert lib.fa_bwd_preprocess(ptr(0), ctypes.c_void_p(0), ptr(2), need, B, Hq, Hkv, N, D, 1, None) == \
+        STATUS["FA_ERR_NULL_POINTER"]
+    assert lib.fa_bwd_main(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), None, None, ptr(5), need,
+                           B, Hq, Hkv, N, 32, 0.1, 1, 1, None) == STATUS["FA_ERR_HEAD_DIM"]
+    # MHA needs dk/dv pointers in the main stage; GQA needs them in the postprocess
+    assert lib.fa_bwd_main(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), None, None, ptr(5),
+                           fa.fa_bwd_workspace_size(B, 2, 2, N, D), B, 2, 2, N, D, 0.1, 1, 1,
+                           None) == STATUS["FA_ERR_NULL_POINTER"]
+    assert lib.fa_bwd_postprocess(ptr(0), None, None, ptr(5), need, B, Hq, Hkv, N, D, 0.1, 1, None) == \
+        STATUS["FA_ERR_NULL_POINTER"]
+    assert lib.fa_bwd_postprocess(ptr(0), ptr(1), ptr(2), ptr(0), need, B, Hq, Hkv, N, D, 0.1, 1, None) == \
+        STATUS["FA_ERR_ALIAS"]
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    with pytest.raises(RuntimeError):
+        fa.fa_fwd(q, q, q)

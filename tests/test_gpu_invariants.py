@@ -1,0 +1,153 @@
+"""GPU checks that do not rely on the oracle's arithmetic: properties of the definition,
+the pages' printed softmax numbers, determinism, error behaviour."""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import exact_attention_fa_amd as fa
+    fa.load_library()
+    return torch, fa
+
+
+def inputs(shape, seed):
+    from exact_attention_fa_amd.inputs import make_inputs
+    import torch
+    return [t.to("cuda") for t in make_inputs(shape, seed)]
+
+
+def test_page_softmax_table_on_gpu(torch_fa):
+    """FlashStieltjes page, 'Why touch softmax' figure data table (softmax column): 64 keys
+    whose scores fall by 0.25 per key.  The GPU's fp32 LSE must reproduce every printed weight
+    through p_j = exp(s_j - LSE), and its fp16 O (with V = identity, so O is the probability
+    row) the weights that fp16 can hold."""
+    torch, fa = torch_fa
+    g = json.load(open(os.path.join(GOLDEN, "softmax_geometric_scores.json")))
+    n = g["n_keys"]
+    q = torch.zeros(1, 1, n, 64, dtype=torch.float16, device="cuda")
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 1, n, 64, dtype=torch.float16, device="cuda")
+    k[0, 0, :, 0] = g["score_step"] * torch.arange(n, dtype=torch.float32, device="cuda")
+    v = torch.eye(n, 64, dtype=torch.float16, device="cuda").reshape(1, 1, n, 64)
+    o, lse = fa.fa_fwd(q, k, v, causal=False, softmax_scale=1.0)
+    torch.cuda.synchronize()
+    lse0 = float(lse[0, 0, 0])
+    row = o[0, 0, 0].float().cpu().numpy()
+    for r in g["rows"]:
+        j = int(round(r["gap"] / -g["score_step"]))
+        p_lse = math.exp(g["score_step"] * j - lse0)
+        assert float(f"{p_lse:.{r['sig_digits']}g}") == pytest.approx(r["softmax"], rel=1e-9), (r, p_lse)
+        if r["softmax"] > 1e-3:
+            assert float(f"{row[j]:.{r['sig_digits']}g}") == pytest.approx(r["softmax"], rel=1e-9), (r, row[j])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_bitwise_deterministic(torch_fa, causal):
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    q, k, v, _ = inputs(Shape(2, 8, 2, 1500, 128, "bf16", causal), 5)
+    o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
+    o2, l2 = fa.fa_fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_gives_value_means(torch_fa, causal):
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    N = 700
+    q, k, v, _ = inputs(Shape(1, 4, 2, N, 64, "fp16", causal), 9)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, softmax_scale=0.0)
+    torch.cuda.synchronize()
+    vv = v.double().cpu().numpy()
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    for h in range(4):
+        vh = vv[0, h // 2]
+        ref = np.cumsum(vh, axis=0) / cnt[:, None] if causal else np.broadcast_to(vh.mean(0), vh.shape)
+        assert np.abs(o[0, h].double().cpu().numpy() - ref).max() < 5e-3
+        assert np.abs(lse[0, h].double().cpu().numpy() - np.log(cnt)).max() < 1e-4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_identities(torch_fa, causal):
+    """sum_j dK_j = 0 (rows of dS sum to zero) and sum_j dV_j = sum over the group of sum_i dO_i."""
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    q, k, v, do = inputs(Shape(1, 8, 2, 1100, 128, "bf16", causal), 13)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    dk64 = dk.double()
+    resid = dk64.sum(dim=2).abs()
+    scale = dk64.abs().sum(dim=2)
+    assert float((resid / scale).max()) < 2e-2
+    tot = do.double().reshape(1, 2, 4, 1100, 128).sum(dim=(2, 3))
+    assert float((dv.double().sum(dim=2) - tot).abs().max()) < 2e-2 * float(tot.abs().max()) + 0.05
+
+
+def test_constant_values_give_zero_dq_dk(torch_fa):
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    q, k, v, do = inputs(Shape(1, 4, 4, 600, 64, "bf16", True), 17)
+    o_r, l_r = fa.fa_fwd(q, k, v, causal=True)
+    dq_r, dk_r, _ = fa.fa_bwd(q, k, v, o_r, do, l_r, causal=True)
+    vc = v[:, :, :1].expand_as(v).contiguous()
+    o, lse = fa.fa_fwd(q, k, vc, causal=True)
+    dq, dk, dv = fa.fa_bwd(q, k, vc, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    assert float((o.float() - vc.float()).abs().max()) < 1e-2
+    assert float(dq.float().abs().max()) < 2e-2 * float(dq_r.float().abs().max())
+    assert float(dk.float().abs().max()) < 2e-2 * float(dk_r.float().abs().max())
+
+
+def test_rejected_call_writes_nothing(torch_fa):
+    torch, fa = torch_fa
+    q = torch.randn(1, 2, 100, 64, device="cuda").half()
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((1, 2, 100), 3.0, device="cuda")
+    with pytest.raises(RuntimeError, match="softmax_scale"):
+        fa.fa_fwd(q, q, q, softmax_scale=-1.0, out=o, lse=lse)
+    with pytest.raises(RuntimeError, match="head dim"):
+        x = torch.randn(1, 2, 100, 96, device="cuda").half()
+        fa.fa_fwd(x, x, x)
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all()) and bool((lse == 3.0).all())
+
+
+def test_no_drift_along_sequence(torch_fa):
+    """'FlashAttention for Tesla P100', section 'Driving a real model': the error of the online
+    softmax does not grow with the position in the sequence.  Binned by position, the largest
+    error of the last bin stays within twice that of the first bin (plus the output rounding)."""
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import WORKLOADS, make_inputs, workload_seed
+    from oracle import attention_forward
+    shape = WORKLOADS["fwd_bf16_long"][0]            # N = 8192
+    q, k, v, _ = make_inputs(shape, workload_seed("fwd_bf16_long", 0), with_grad=False)
+    o, _ = fa.fa_fwd(q[:, :1].cuda(), k[:, :1].cuda(), v[:, :1].cuda())
+    torch.cuda.synchronize()
+    rows = np.arange(0, shape.N, 32)
+    f = lambda t: t.double().cpu().numpy()
+    o_ref, _ = attention_forward(f(q[:, :1]), f(k[:, :1]), f(v[:, :1]), shape.scale, False, rows=rows)
+    err = np.abs(f(o)[0, 0, rows] - o_ref[0, 0]).max(axis=-1)
+    bins = err.reshape(8, -1).max(axis=1)
+    log("per-bin max error", bins)
+    assert bins[-1] <= 2 * bins[0] + 2e-3

@@ -1,0 +1,111 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Small shapes are compared element by element on every output; the full-size workloads
+are run exactly as the benchmark launches them and compared on sampled outputs that the
+oracle recomputes one (batch, kv-group) unit at a time.
+"""
+import sys
+import zlib
+
+import pytest
+
+from exact_attention_fa_amd.inputs import WORKLOADS, Shape, workload_seed
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import exact_attention_fa_amd as fa
+    fa.load_library()
+
+
+# ------------------------------------------------------------ tiny workload (full oracle)
+
+@pytest.mark.parametrize("variant", [0, 1], ids=["noncausal", "causal"])
+def test_tiny_fp16_full(variant):
+    from parity_util import full_check
+    shape = WORKLOADS["tiny_fp16"][variant]
+    log("tiny", shape)
+    errs = full_check(shape, workload_seed("tiny_fp16", variant))
+    log("  errors", errs)
+
+
+# ------------------------------------------------ small shapes spanning tiles and tails
+
+SMALL = [
+    # (B, Hq, Hkv, N, D)
+    (1, 2, 2, 1, 64),        # single token
+    (1, 2, 1, 7, 128),       # shorter than one MFMA block
+    (2, 4, 1, 129, 64),      # MQA, one row past a tile
+    (1, 6, 2, 333, 128),     # GQA 3:1, ragged
+    (1, 2, 2, 640, 64),      # several whole tiles
+    (2, 4, 4, 517, 128),     # MHA, ragged, B=2
+]
+
+
+@pytest.mark.parametrize("dims", SMALL, ids=[f"B{b}H{hq}/{hk}N{n}D{d}" for b, hq, hk, n, d in SMALL])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["nc", "causal"])
+def test_small_full(dims, dtype, causal):
+    from parity_util import full_check
+    B, Hq, Hkv, N, D = dims
+    shape = Shape(B, Hq, Hkv, N, D, dtype, causal)
+    log("small", shape)
+    full_check(shape, seed=zlib.crc32(repr((dims, dtype, causal)).encode()) % (1 << 31))
+
+
+def test_nondefault_scale_full():
+    from parity_util import full_check
+    for scale in (0.0, 0.05, 0.4):
+        shape = Shape(1, 4, 2, 300, 64, "bf16", True)
+        log("scale", scale)
+        full_check(shape, seed=77, scale=scale)
+
+
+# --------------------------------------------------- the full-size workloads (sampled)
+
+def test_fwd_bf16_n4096_sampled():
+    from parity_util import sampled_check
+    shape = WORKLOADS["fwd_bf16_n4096"][0]
+    log("workload", shape)
+    errs, _ = sampled_check(shape, workload_seed("fwd_bf16_n4096", 0), units=[(0, 0), (1, 7), (3, 15)],
+                            n_rows=48, backward=False)
+    log("  errors", errs)
+
+
+@pytest.mark.parametrize("variant", [0, 1], ids=["n8192", "n16384"])
+def test_fwd_bf16_long_sampled(variant):
+    from parity_util import sampled_check
+    shape = WORKLOADS["fwd_bf16_long"][variant]
+    log("workload", shape)
+    errs, _ = sampled_check(shape, workload_seed("fwd_bf16_long", variant), units=[(0, 0), (0, 11)],
+                            n_rows=48, backward=False)
+    log("  errors", errs)
+
+
+@pytest.mark.parametrize("variant", range(6), ids=[f"N{s.N}D{s.D}" for s in WORKLOADS["gqa_causal_fp16"]])
+def test_gqa_causal_fp16_sampled(variant):
+    from parity_util import sampled_check
+    shape = WORKLOADS["gqa_causal_fp16"][variant]
+    log("workload", shape)
+    errs, _ = sampled_check(shape, workload_seed("gqa_causal_fp16", variant), units=[(0, 0), (0, 3)],
+                            n_rows=64, backward=True)
+    log("  errors", errs)
+
+
+def test_causal_long_bf16_sampled():
+    from parity_util import sampled_check
+    shape = WORKLOADS["causal_long_bf16"][0]
+    log("workload", shape)
+    errs, _ = sampled_check(shape, workload_seed("causal_long_bf16", 0), units=[(0, 5)],
+                            n_rows=48, backward=True)
+    log("  errors", errs)
