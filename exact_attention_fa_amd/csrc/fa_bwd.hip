@@ -167,19 +167,11 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     else if (tid < 2 * BQ) sD[tid - BQ] = lreg;
   };
 
-  if (qt0 < n_qt) gload(qt0);
-  for (int qt = qt0; qt < n_qt; ++qt) {
-    const int q0 = qt * BQ;
-    __syncthreads();  // previous tile's LDS reads are finished
-    lstore();
-    __syncthreads();
-    if (qt + 1 < n_qt) gload(qt + 1);
-
-    const bool need_mask = (kw0 + 32 > N) || (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31);
-
-    // ---- recompute P, form dP and dS; register i of block qb <-> query
-    //      q0 + qb*32 + (i/8)*16 + g*8 + i%8, key `key`
-    u32x4 pa[2][2], dsa[2][2];
+  // Recompute P and form dS for the 64-query tile in LDS; register i of query block qb
+  // <-> query q0 + qb*32 + (i/8)*16 + g*8 + i%8, key `key`.  P and dS come back rounded
+  // to the input type as A operands (k-slot j of (qb, t2) = query q0 + qb*32 + t2*16 + g*8
+  // + j), and dS^T is also written to LDS for the dQ product.
+  auto p_ds = [&](const bool masked, const int q0, u32x4 (&pa)[2][2], u32x4 (&dsa)[2][2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -189,6 +181,14 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk)
         dp = TR::mfma(lds_read8<HD>(sdO, qb * 32 + perm_rows(c), kk * 16 + g * 8), vr[kk], dp);
+      // masked scores become -inf, so exp2 (with c2 > 0) makes them exact zeros
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = q0 + qb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          if (key >= N || q >= N || (CAUSAL && key > q)) s[i] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int r0 = qb * 32 + t2 * 16 + g * 8;
@@ -202,11 +202,7 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           const int i = t2 * 8 + j;
           const float lse2 = j < 4 ? l0[j] : l1[j - 4];
           const float dd = j < 4 ? d0[j] : d1[j - 4];
-          float pv = fast_exp2(fmaf(s[i], c2, -lse2));
-          if (need_mask) {
-            const int q = q0 + r0 + j;
-            if (key >= N || q >= N || (CAUSAL && key > q)) pv = 0.f;
-          }
+          const float pv = fast_exp2(fmaf(s[i], c2, -lse2));
           p[j] = pv;
           ds[j] = pv * (dp[i] - dd);
         }
@@ -217,6 +213,20 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         lds_write8<BQ>(sdS, wave * 32 + c, r0, dsa[qb][t2]);
       }
     }
+  };
+
+  if (qt0 < n_qt) gload(qt0);
+  for (int qt = qt0; qt < n_qt; ++qt) {
+    const int q0 = qt * BQ;
+    __syncthreads();  // previous tile's LDS reads are finished
+    lstore();
+    __syncthreads();
+    if (qt + 1 < n_qt) gload(qt + 1);
+
+    // Masks only on the tiles that cross the diagonal or a ragged edge; the common case is
+    // compiled without any mask code.
+    u32x4 pa[2][2], dsa[2][2];
+    p_ds((kw0 + 32 > N) || (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31), q0, pa, dsa);
 
     // ---- dV += P^T dO and dK += dS^T Q (the rounded P / dS registers are the A operands)
 #pragma unroll
@@ -246,10 +256,16 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           const u32x4 bk = lds_read_tr8<HD>(sK, ks * 16, db * 32, lane);
           dq = TR::mfma(a, bk, dq);
         }
+        float* const dst = dQh + (size_t)(q0 + qb * 32 + g * 4) * HD + db * 32 + c;
+        if (q0 + BQ <= N) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q0 + qb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          if (q < N) unsafeAtomicAdd(dQh + (size_t)q * HD + db * 32 + c, dq[i]);
+          for (int i = 0; i < 16; ++i) unsafeAtomicAdd(dst + ((i >> 2) * 8 + (i & 3)) * HD, dq[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int q = q0 + qb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+            if (q < N) unsafeAtomicAdd(dst + ((i >> 2) * 8 + (i & 3)) * HD, dq[i]);
+          }
         }
       }
     }
@@ -339,7 +355,7 @@ hipError_t main_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse,
                      reinterpret_cast<const float*>(a.ws + w.delta), reinterpret_cast<float*>(a.ws + w.dq_acc),
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dkp, dvp, (int)a.Hq,
-                     (int)a.Hkv, (int)a.N, n_kt, a.scale * kLog2e, a.scale);
+                     (int)a.Hkv, (int)a.N, n_kt, a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f, a.scale);
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ namespace {
 constexpr int kFwdBR = 128;  // query rows per workgroup
 constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kThreads = 256;
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 of the largest probability)
 
 template <typename TR, int HD, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -109,7 +110,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int kv0 = t * BC;
     if (CAUSAL && kv0 > qw0 + 31) continue;  // tile lies above the diagonal for this wave
 
-    // ---- S^T = K Q^T: register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
+    // register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -120,25 +121,22 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         s[kb] = TR::mfma(a, qf[kk], s[kb]);
       }
     }
-
-    // ---- masks (ragged tail, causal diagonal): only on tiles that need them
-    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-    uint32_t dead = 0;
-    if (need_mask) {
+    // Masks only on the ragged last tile and on tiles crossing the diagonal (a uniform
+    // branch): masked scores become -inf, so exp2 (with c2 > 0) turns them into exact zeros.
+    if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-          const bool off = key >= N || (CAUSAL && key > qi);
-          if (off) {
-            dead |= 1u << (kb * 16 + i);
-            s[kb][i] = -INFINITY;
-          }
+          if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
         }
     }
 
-    // ---- online softmax (scores in raw units; c2 = scale * log2(e) >= 0)
+    // Online softmax in raw-score units (c2 = scale * log2(e) > 0).  The reference max
+    // m_run is only moved when the tile max exceeds it by more than 2^kRescaleLog2 in the
+    // exp2 domain (always on the first tile); otherwise probabilities up to 2^kRescaleLog2
+    // are accumulated against the stale reference, which is exact because O and l share it.
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -146,24 +144,27 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = pair_max(mx);
     const float m_new = fmaxf(m_run, mx);  // finite: key 0 of tile 0 is visible to every row
-    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c2);
-    const float mb = m_new * c2;
+    const bool grow = (m_run == -INFINITY) || ((m_new - m_run) * c2 > kRescaleLog2);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    const float mb = m_run * c2;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s[kb][i], c2, -mb));
-        if (need_mask && ((dead >> (kb * 16 + i)) & 1u)) p = 0.f;
+        const float p = fast_exp2(fmaf(s[kb][i], c2, -mb));
         s[kb][i] = p;
         rs += p;
       }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    l_run += rs;
 
-    // ---- P^T operands: slot j of (kb, t2) = P for key kv0 + kb*32 + t2*16 + g*8 + j
+    // P^T operands: slot j of (kb, t2) = P for key kv0 + kb*32 + t2*16 + g*8 + j
     u32x4 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -174,7 +175,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                            TR::pack(s[kb][i0 + 4], s[kb][i0 + 5]), TR::pack(s[kb][i0 + 6], s[kb][i0 + 7])};
       }
 
-    // ---- O^T += V^T P^T  (A = V^T rows d, k = keys, read transposed from the V tile)
+    // O^T += V^T P^T  (A = V^T: rows d, k = keys, read transposed from the V tile)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -208,7 +209,9 @@ template <typename TR, int HD, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a) {
   const int n_qt = (int)((a.N + kFwdBR - 1) / kFwdBR);
   const long long blocks = a.B * a.Hq * (long long)n_qt;
-  const float c2 = a.scale * kLog2e;
+  // c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
+  // becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
+  const float c2 = a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f;
   hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,

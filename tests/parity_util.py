@@ -47,11 +47,24 @@ def rel_err(g, ref):
     return float(np.abs(g - ref).max() / max(np.abs(ref).max(), GRAD_FLOOR))
 
 
-def assert_fwd_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
+def derived_o_tol(v, dtype: str) -> float:
+    """Bound on |O_gpu - O_ref| from the arithmetic, for scales other than 1/sqrt(D).
+
+    P is rounded to the input type as an MFMA operand (relative error <= u/2 per weight, so
+    |dO| <= (u/2) max|V|) and O is rounded once on output (<= u |O| <= u max|V|), with u the
+    unit roundoff step 2^-8 (bf16) or 2^-11 (fp16).  Peaked softmax rows (large scales) push
+    |O| towards max|V|, where the fixed 1e-2 bound of the configured workloads no longer
+    leaves room for the output rounding alone.
+    """
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    return max(TOL_O, 1.5 * u * float(np.abs(v).max()))
+
+
+def assert_fwd_close(o_gpu, lse_gpu, o_ref, lse_ref, what="", tol_o=TOL_O):
     eo = float(np.abs(o_gpu - o_ref).max())
     el = float(np.abs(lse_gpu - lse_ref).max())
     assert np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all(), what
-    assert eo <= TOL_O, f"{what}: O max-abs error {eo:.3e} > {TOL_O}"
+    assert eo <= tol_o, f"{what}: O max-abs error {eo:.3e} > {tol_o:.3e}"
     assert el <= TOL_LSE, f"{what}: LSE max-abs error {el:.3e} > {TOL_LSE}"
     return eo, el
 
@@ -64,12 +77,18 @@ def assert_grad_close(g, ref, name, what=""):
 
 
 def full_check(shape: Shape, seed: int, backward: bool = True, scale=None):
-    """Element-by-element comparison of every output against the oracle."""
+    """Element-by-element comparison of every output against the oracle.
+
+    At the workloads' scale 1/sqrt(D) the O bound is the fixed 1e-2; for other scales it is
+    the bound derived from the arithmetic (``derived_o_tol``).
+    """
+    default_scale = scale is None
     scale = shape.scale if scale is None else scale
     q, k, v, do = make_inputs(shape, seed)
     o, lse = gpu_forward(q, k, v, shape.causal, scale)
     o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v), scale, shape.causal)
-    errs = dict(zip(("o", "lse"), assert_fwd_close(f64(o), f64(lse), o_ref, lse_ref, str(shape))))
+    tol_o = TOL_O if default_scale else derived_o_tol(f64(v), shape.dtype)
+    errs = dict(zip(("o", "lse"), assert_fwd_close(f64(o), f64(lse), o_ref, lse_ref, str(shape), tol_o)))
     if backward:
         dq, dk, dv = gpu_backward(q, k, v, o, do, lse, shape.causal, scale)
         dq_r, dk_r, dv_r = attention_backward(f64(q), f64(k), f64(v), f64(do), scale, shape.causal)
