@@ -127,7 +127,7 @@ def main():
         fa.fa_fwd(q, k, v, causal=causal, softmax_scale=scale, out=o, lse=lse)
         if ev is not None:
             ev[1].record(stream)
-        fa.fa_bwd_preprocess(o, do, ws, Hkv)
+        fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
         if ev is not None:
             ev[2].record(stream)
         fa.fa_bwd_main(q, k, v, do, lse, dk, dv, ws, causal=causal, softmax_scale=scale)

@@ -43,7 +43,7 @@ _SIGS = {
     "fa_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                 _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
                ctypes.c_int),
-    "fa_bwd_preprocess": ([_vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
+    "fa_bwd_preprocess": ([_vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
                            ctypes.c_int, _vp], ctypes.c_int),
     "fa_bwd_main": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                      _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
@@ -181,10 +181,10 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale=None, worksp
     return dq, dk, dv
 
 
-def fa_bwd_preprocess(o, do, workspace, Hkv: int):
+def fa_bwd_preprocess(o, do, lse, workspace, Hkv: int):
     B, Hq, N, D = o.shape
     _require(o, do, dtype=o.dtype)
-    rc = load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(workspace),
+    rc = load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(),
                                           B, Hq, Hkv, N, D, _dtype_code(o), _stream(o))
     _check(rc, "fa_bwd_preprocess")

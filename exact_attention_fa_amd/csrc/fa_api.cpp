@@ -75,6 +75,8 @@ BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long
   off += round_up(rows * (size_t)D * 4);
   w.delta = off;
   off += round_up(rows * 4);
+  w.lse2 = off;
+  off += round_up(rows * 4);
   if (Hq != Hkv) {
     w.dk_part = off;
     off += round_up(rows * (size_t)D * 4);
@@ -177,16 +179,17 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return status_of(launch_bwd_postprocess(a));
 }
 
-int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int64_t B,
-                      int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype, void* stream) {
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace, size_t workspace_bytes,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype, void* stream) {
   FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
   FA_TRY(check_ptr(o, 16));
   FA_TRY(check_ptr(dout, 16));
+  FA_TRY(check_ptr(lse, 4));
   const size_t qb = (size_t)(B * Hq * N * D) * 2;
-  const Range r[] = {{o, qb, false}, {dout, qb, false},
+  const Range r[] = {{o, qb, false}, {dout, qb, false}, {lse, (size_t)(B * Hq * N) * 4, false},
                      {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, true}};
-  FA_TRY(check_alias(r, 3));
-  const BwdArgs a = make_bwd_args(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, workspace,
+  FA_TRY(check_alias(r, 4));
+  const BwdArgs a = make_bwd_args(nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr, workspace,
                                   B, Hq, Hkv, N, D, 1.f, 0, dtype, stream);
   return status_of(launch_bwd_preprocess(a));
 }

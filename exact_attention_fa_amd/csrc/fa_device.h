@@ -85,52 +85,69 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 
 // ---------------------------------------------------------------- LDS tiles
 //
-// A tile is a row-major array of 16-bit elements with ROW (64 or 128) elements per row,
-// packed into 256-byte bank lines (one row of 128, or two rows of 64).  The 16-byte
-// chunk index inside a bank line is XOR-swizzled with a function of the line index so
-// that both access patterns used on tiles are free of bank conflicts:
-//   * ds_read_b128 / ds_write_b128 by 16 lanes on 16 distinct rows (mod 16), same chunk;
-//   * ds_read_b64_tr_b16 by 32 lanes on 4 consecutive rows and 4 consecutive chunks.
-template <int ROW>
-__device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
-  static_assert(ROW == 64 || ROW == 128, "tile rows hold 64 or 128 elements");
-  if constexpr (ROW == 128) {
-    const uint32_t f = ((r & 3u) << 2) | ((r >> 2) & 3u);
-    return r * 256u + ((c ^ f) << 4);
-  } else {
-    const uint32_t line = r >> 1;
-    const uint32_t slot = ((r & 1u) << 3) | c;
-    const uint32_t f = ((line & 1u) << 2) | ((line >> 1) & 3u);
-    return line * 256u + ((slot ^ f) << 4);
-  }
+// A tile of R rows x W 16-bit columns (W = 64 or 128) is stored as W/32 "slices" of
+// R rows x 32 columns; a slice row is 64 bytes (four 16-byte chunks) and four rows share a
+// 256-byte bank line.  The chunk index is XORed with bits 2..3 of the row.  This makes both
+// access patterns used on tiles free of bank conflicts (64 banks x 4 bytes):
+//   * 16-byte reads/writes by 16 lanes on 16 distinct rows (mod 16), same column;
+//   * ds_read_b64_tr_b16 by 32 lanes on 4 consecutive rows x 32 consecutive columns;
+// and it keeps every compile-time part of an address additive: for rows rb + lr (rb a
+// multiple of 16) and columns cb + lc (cb a multiple of 32, lc < 32),
+//   sl_off(rb + lr, cb + lc) = sl_off(rb, cb) + sl_off(lr, lc),
+// so a lane computes its offsets once and every read uses an immediate offset.
+template <int R>
+__device__ __forceinline__ uint32_t sl_off(uint32_t r, uint32_t col) {
+  return (col >> 5) * (uint32_t)(R * 64) + r * 64u + ((((col >> 3) & 3u) ^ ((r >> 2) & 3u)) << 4) +
+         (col & 7u) * 2u;
 }
 
-template <int ROW>
-__device__ __forceinline__ void lds_write8(char* tile, int row, int col, u32x4 v) {
-  *reinterpret_cast<u32x4*>(tile + lds_off<ROW>(row, col >> 3)) = v;
+// Inverse for 16-byte chunks: (row, column) of the chunk stored at 16-byte position P.  The
+// direct global->LDS loads write lane l's 16 bytes at base + 16*l, so lane l of the load that
+// fills positions [64*i, 64*i + 64) fetches the chunk that belongs at position 64*i + l.
+template <int R>
+__device__ __forceinline__ void sl_pos_to_rc(uint32_t P, int& row, int& col) {
+  const uint32_t slice = P / (uint32_t)(R * 4), q = P % (uint32_t)(R * 4);
+  const uint32_t r = q >> 2, pc = q & 3u;
+  row = (int)r;
+  col = (int)(slice * 32u + ((pc ^ ((r >> 2) & 3u)) << 3));
 }
 
-// Eight consecutive elements T[row][col .. col+7] (col a multiple of 8).
-template <int ROW>
-__device__ __forceinline__ u32x4 lds_read8(const char* tile, int row, int col) {
-  return *reinterpret_cast<const u32x4*>(tile + lds_off<ROW>(row, col >> 3));
+// Direct global -> LDS copy (global_load_lds_dwordx4 / _dword): every active lane fetches
+// BYTES from its own address `src`; lane l's data lands at lds_base + BYTES * l.  Completion
+// is tracked by vmcnt.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(const void* src, char* lds_base) {
+  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte direct loads");
+  auto* dst = (__attribute__((address_space(3))) void*)lds_base;
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
-// Transposed operand fragment: slot j of lane l receives T[rowbase + g*8 + j][colbase + c]
-// (c = l % 32, g = l / 32), i.e. eight elements down a column, as the MFMA A or B operand
-// wants when the contraction index runs along the tile's rows.  Uses two
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the
-// 8-byte words addressed by lanes 4r + i/4 (r = 0..3), in slot r.
-template <int ROW>
-__device__ __forceinline__ u32x4 lds_read_tr8(const char* tile, int rowbase, int colbase, int lane) {
+__device__ __forceinline__ u32x4 lds_ld128(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void lds_st128(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Lane offsets of the transposed-operand read (see lds_tr8): rows lr and lr + 4, column lc.
+struct TrLane {
+  uint32_t r0, r4;
+};
+__device__ __forceinline__ TrLane tr_lane(int lane) {
   const int grp = lane >> 4, i = lane & 15;
-  const int row = rowbase + (grp >> 1) * 8 + (i >> 2);
-  const int col = colbase + (grp & 1) * 16 + (i & 3) * 4;
-  const uint32_t sub = (uint32_t)(col & 4) << 1;  // byte offset of the word inside its chunk
-  const lds_s16x4* p0 = (const lds_s16x4*)(tile + lds_off<ROW>(row, col >> 3) + sub);
-  const lds_s16x4* p1 = (const lds_s16x4*)(tile + lds_off<ROW>(row + 4, col >> 3) + sub);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+  const int lr = (grp >> 1) * 8 + (i >> 2);
+  const int lc = (grp & 1) * 16 + (i & 3) * 4;
+  return TrLane{sl_off<16>(lr, lc), sl_off<16>(lr + 4, lc)};
+}
+
+// Transposed operand fragment at tile position p (= tile + sl_off(rowbase, colbase), rowbase
+// a multiple of 16, colbase a multiple of 32): slot j of lane l receives
+// T[rowbase + g*8 + j][colbase + c] (c = l % 32, g = l / 32), eight elements down a column,
+// as an MFMA operand needs when the contraction runs along the tile's rows.  Two
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte
+// words addressed by lanes 4r + i/4 (r = 0..3), in slot r.
+__device__ __forceinline__ u32x4 lds_tr8(const char* p, TrLane t) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + t.r0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + t.r4));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
   return r;
@@ -160,5 +177,24 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- synchronisation
+
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations only.  (HIP's
+// __syncthreads also drains every outstanding global load, store and atomic.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(N): wait until at most N of this wave's vector-memory operations are
+// outstanding.  On gfx9-family targets loads, stores, atomics and direct-to-LDS loads share
+// this counter and retire in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 }  // namespace fa

@@ -11,14 +11,15 @@
 //
 // gfx950 realisation:
 //   * 256 threads = 4 waves; a wave owns 32 query rows (BR = 128 rows per workgroup).
-//   * K/V tiles of BC = 64 keys staged through LDS (swizzled row-major), prefetched into
-//     registers one tile ahead so global latency overlaps the MFMA/softmax work.
+//   * K/V tiles of BC = 64 keys are copied global -> LDS by direct loads into a double
+//     buffer, one tile ahead of the compute, with no register staging.
 //   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16: each lane then
 //     owns one query column, its row max and row sum are in-lane reductions plus one
 //     v_permlane32_swap, and the bf16/fp16-rounded probabilities in registers are already
 //     the B operand of O^T += V^T P^T.  V^T comes from the row-major V tile through
 //     ds_read_b64_tr_b16.
-//   * exp2 on the VALU with scale*log2(e) folded into one FMA per score.
+//   * exp2 on the VALU with scale*log2(e) folded into one FMA per score; the running max
+//     is moved (and O, l rescaled) only when it grows by more than 2^8.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -37,19 +38,19 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
            const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
            int Hq, int Hkv, int N, int n_qt, float c2, float scale) {
   constexpr int BR = kFwdBR, BC = kFwdBC;
-  constexpr int KST = HD / 16;                 // k-steps of S^T over the head dim
-  constexpr int DB = HD / 32;                  // 32-row blocks of O^T
-  constexpr int TILE = BC * HD * 2;            // bytes of one K or V tile
-  constexpr int CPR = HD / 8;                  // 16-byte chunks per row
-  constexpr int CH = BC * CPR / kThreads;      // chunks per thread per tile
-  static_assert(CH * kThreads == BC * CPR, "tile must split evenly over the workgroup");
+  constexpr int KST = HD / 16;              // k-steps of S^T over the head dim
+  constexpr int DB = HD / 32;               // 32-row blocks of O^T
+  constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
+  constexpr int TI = TILE / 1024 / 4;       // 1 KB direct loads per wave per tile
+  static_assert(TI * 4096 == TILE, "tile must split into 1 KB loads over 4 waves");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2], V[2]
   char* const sK = smem;
-  char* const sV = smem + TILE;
+  char* const sV = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
 
   const int job = xcd_remap(blockIdx.x, gridDim.x);
@@ -65,64 +66,62 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int qw0 = qt * BR + wave * 32;  // first query row of this wave
   const int qi = qw0 + c;               // the query row this lane's column belongs to
 
+  int kv_end = (N + BC - 1) / BC;
+  if (CAUSAL) kv_end = (min(N, (qt + 1) * BR) - 1) / BC + 1;
+
+  // Direct loads of K/V tile t into buffer `buf`; keys past the end read key N-1 (finite
+  // data that the masks then exclude).
+  auto issue = [&](int t, int buf) {
+#pragma unroll
+    for (int r = 0; r < TI; ++r) {
+      const int blk = wave * TI + r;
+      int row, col;
+      sl_pos_to_rc<BC>((uint32_t)(blk * 64 + lane), row, col);
+      const size_t src = (size_t)min(t * BC + row, N - 1) * HD + col;
+      dma_to_lds<16>(Kh + src, sK + buf * TILE + blk * 1024);
+      dma_to_lds<16>(Vh + src, sV + buf * TILE + blk * 1024);
+    }
+  };
+  issue(0, 0);
+
   // Q fragments: B operand of S^T = K Q^T (slot j of k-step kk = Q[qi][kk*16 + g*8 + j]).
   u32x4 qf[KST];
 #pragma unroll
   for (int kk = 0; kk < KST; ++kk) qf[kk] = ld16_if(Qh + (size_t)qi * HD + kk * 16 + g * 8, qi < N);
 
+  // Per-lane LDS offsets.  K rows are read in the permuted order, so register i of an S^T
+  // block is key (i/8)*16 + g*8 + i%8; one offset per k-step parity.
+  const uint32_t koff[2] = {sl_off<BC>(perm_rows(c), g * 8), sl_off<BC>(perm_rows(c), 16 + g * 8)};
+  const TrLane trl = tr_lane(lane);
+
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of raw scores for query qi
+  float m_run = -INFINITY;  // running (reference) max of raw scores for query qi
   float l_run = 0.f;        // this lane's share of the running sum of 2^((s - m) * c2)
 
-  int kv_end = (N + BC - 1) / BC;
-  if (CAUSAL) kv_end = (min(N, (qt + 1) * BR) - 1) / BC + 1;
-
-  u32x4 kreg[CH], vreg[CH];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      const int cid = tid + kThreads * r;
-      const int row = cid / CPR, ch = cid % CPR;
-      const int key = t * BC + row;
-      kreg[r] = ld16_if(Kh + (size_t)key * HD + ch * 8, key < N);
-      vreg[r] = ld16_if(Vh + (size_t)key * HD + ch * 8, key < N);
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      const int cid = tid + kThreads * r;
-      const int row = cid / CPR, ch = cid % CPR;
-      lds_write8<HD>(sK, row, ch * 8, kreg[r]);
-      lds_write8<HD>(sV, row, ch * 8, vreg[r]);
-    }
-  };
-
-  gload(0);
   for (int t = 0; t < kv_end; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    lstore();
-    __syncthreads();
-    if (t + 1 < kv_end) gload(t + 1);
+    wait_vmcnt<0>();  // this wave's share of tile t has landed
+    lds_barrier();    // ... and everyone's; everyone is also done with tile t-1
+    if (t + 1 < kv_end) issue(t + 1, (t + 1) & 1);
 
     const int kv0 = t * BC;
     if (CAUSAL && kv0 > qw0 + 31) continue;  // tile lies above the diagonal for this wave
+    const char* const tK = sK + (t & 1) * TILE;
+    const char* const tV = sV + (t & 1) * TILE;
 
-    // register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
+    // ---- S^T = K Q^T: register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk) {
-        const u32x4 a = lds_read8<HD>(sK, kb * 32 + perm_rows(c), kk * 16 + g * 8);
-        s[kb] = TR::mfma(a, qf[kk], s[kb]);
-      }
+      for (int kk = 0; kk < KST; ++kk)
+        s[kb] = TR::mfma(lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]), qf[kk], s[kb]);
     }
-    // Masks only on the ragged last tile and on tiles crossing the diagonal (a uniform
-    // branch): masked scores become -inf, so exp2 (with c2 > 0) turns them into exact zeros.
+
+    // ---- masks only on the ragged last tile and tiles crossing the diagonal (a uniform
+    //      branch): masked scores become -inf, so exp2 (with c2 > 0) makes exact zeros.
     if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -133,10 +132,10 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
     }
 
-    // Online softmax in raw-score units (c2 = scale * log2(e) > 0).  The reference max
-    // m_run is only moved when the tile max exceeds it by more than 2^kRescaleLog2 in the
-    // exp2 domain (always on the first tile); otherwise probabilities up to 2^kRescaleLog2
-    // are accumulated against the stale reference, which is exact because O and l share it.
+    // ---- online softmax in raw-score units (c2 = scale * log2(e) > 0).  The reference max
+    //      moves only when the tile max exceeds it by more than 2^kRescaleLog2 in the exp2
+    //      domain (always on the first tile); otherwise probabilities up to 2^kRescaleLog2
+    //      accumulate against the stale reference, exact because O and l share it.
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -164,7 +163,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
     l_run += rs;
 
-    // P^T operands: slot j of (kb, t2) = P for key kv0 + kb*32 + t2*16 + g*8 + j
+    // ---- P^T operands: slot j of (kb, t2) = P for key kv0 + kb*32 + t2*16 + g*8 + j
     u32x4 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -175,16 +174,14 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                            TR::pack(s[kb][i0 + 4], s[kb][i0 + 5]), TR::pack(s[kb][i0 + 6], s[kb][i0 + 7])};
       }
 
-    // O^T += V^T P^T  (A = V^T: rows d, k = keys, read transposed from the V tile)
+    // ---- O^T += V^T P^T  (A = V^T: rows d, k = keys, read transposed from the V tile)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const u32x4 a = lds_read_tr8<HD>(sV, kb * 32 + t2 * 16, db * 32, lane);
-          acc[db] = TR::mfma(a, pb[kb][t2], acc[db]);
-        }
+        for (int t2 = 0; t2 < 2; ++t2)
+          acc[db] = TR::mfma(lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl), pb[kb][t2], acc[db]);
   }
 
   // ---- epilogue: normalise, write O (input dtype, RNE) and LSE (natural log, fp32)

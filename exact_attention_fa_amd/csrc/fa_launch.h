@@ -25,6 +25,7 @@ struct FwdArgs {
 struct BwdWorkspace {
   size_t dq_acc;   // fp32 (B, Hq, N, D): dQ accumulated over K/V tiles
   size_t delta;    // fp32 (B, Hq, N): D = rowsum(dO * O)
+  size_t lse2;     // fp32 (B, Hq, N): LSE * log2(e)
   size_t dk_part;  // fp32 (B, Hq, N, D): per-query-head dK partials (only when Hq > Hkv)
   size_t dv_part;  // fp32 (B, Hq, N, D): per-query-head dV partials (only when Hq > Hkv)
   size_t total;

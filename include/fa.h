@@ -90,8 +90,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            float softmax_scale, int causal, int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs (fp32 dQ accumulator, the D vector and, when
- * Hq > Hkv, per-query-head dK/dV partials).  Returns 0 for invalid shapes.
+ * Bytes of device workspace fa_bwd needs (fp32 dQ accumulator, the D and LSE*log2(e)
+ * vectors and, when Hq > Hkv, per-query-head dK/dV partials).  Returns 0 for invalid shapes.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D);
 
@@ -112,17 +112,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * The three stages of fa_bwd, exported so a caller (or a profiler harness) can place
  * events between them.  Running them in this order on one stream with the same
  * workspace is exactly fa_bwd.
- *   fa_bwd_preprocess:  workspace.D = rowsum(dout * o) in fp32; zeroes the dQ accumulator.
- *   fa_bwd_main:        recomputes P, adds scale-free dS K into the dQ accumulator, and
- *                       writes dk/dv (Hq == Hkv) or fp32 per-query-head partials into the
- *                       workspace (Hq > Hkv).  Needs the preprocess results.
+ *   fa_bwd_preprocess:  D = rowsum(dout * o) and LSE * log2(e) into the workspace (fp32);
+ *                       zeroes the dQ accumulator.
+ *   fa_bwd_main:        recomputes P from the workspace's LSE * log2(e), adds scale-free
+ *                       dS K into the dQ accumulator, and writes dk/dv (Hq == Hkv) or fp32
+ *                       per-query-head partials into the workspace (Hq > Hkv).  Needs the
+ *                       preprocess results; its lse argument is only validated.
  *   fa_bwd_postprocess: dq = scale * accumulator in `dtype`; for Hq > Hkv also sums the
  *                       dK/dV partials over each group into dk/dv.
  * Arguments a stage does not use may be NULL (and are then not checked).
  */
-int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
-                      int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
-                      void* stream);
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
+                      size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                      int dtype, void* stream);
 int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                 void* dk, void* dv, void* workspace, size_t workspace_bytes,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,

@@ -103,7 +103,7 @@ def test_workspace_size(lib):
     B, Hq, Hkv, N, D = 1, 16, 4, 4000, 128
     up = lambda x: (x + 255) // 256 * 256
     rows = B * Hq * N
-    mha = up(rows * D * 4) + up(rows * 4)
+    mha = up(rows * D * 4) + 2 * up(rows * 4)
     assert fa.fa_bwd_workspace_size(B, Hq, Hq, N, D) == mha
     assert fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D) == mha + 2 * up(rows * D * 4)
     assert fa.fa_bwd_workspace_size(0, Hq, Hkv, N, D) == 0
@@ -135,10 +135,12 @@ def test_bwd_rejects(lib):
 def test_stage_entry_points_reject(lib):
     B, Hq, Hkv, N, D = 1, 4, 2, 100, 128
     need = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D)
-    assert lib.fa_bwd_preprocess(ptr(0), ptr(1), ptr(2), need - 16, B, Hq, Hkv, N, D, 1, None) == \
+    assert lib.fa_bwd_preprocess(ptr(0), ptr(1), ptr(3), ptr(2), need - 16, B, Hq, Hkv, N, D, 1, None) == \
         STATUS["FA_ERR_WORKSPACE"]
-    assert lib.fa_bwd_preprocess(ptr(0), ctypes.c_void_p(0), ptr(2), need, B, Hq, Hkv, N, D, 1, None) == \
+    assert lib.fa_bwd_preprocess(ptr(0), ctypes.c_void_p(0), ptr(3), ptr(2), need, B, Hq, Hkv, N, D, 1, None) == \
         STATUS["FA_ERR_NULL_POINTER"]
+    assert lib.fa_bwd_preprocess(ptr(0), ptr(1), ctypes.c_void_p(A + 2), ptr(2), need, B, Hq, Hkv, N, D, 1,
+                                 None) == STATUS["FA_ERR_ALIGNMENT"]
     assert lib.fa_bwd_main(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), None, None, ptr(5), need,
                            B, Hq, Hkv, N, 32, 0.1, 1, 1, None) == STATUS["FA_ERR_HEAD_DIM"]
     # MHA needs dk/dv pointers in the main stage; GQA needs them in the postprocess
