@@ -119,7 +119,7 @@ def main():
     causal, scale = shape.causal, shape.scale
     stream = torch.cuda.current_stream(dev)
 
-    kernels = ["fwd", "bwd_preprocess", "bwd_main", "bwd_postprocess"]
+    kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_postprocess"]
 
     def step(ev=None):
         if ev is not None:
@@ -130,19 +130,22 @@ def main():
         fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
         if ev is not None:
             ev[2].record(stream)
-        fa.fa_bwd_main(q, k, v, do, lse, dk, dv, ws, causal=causal, softmax_scale=scale)
+        fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=causal, softmax_scale=scale)
         if ev is not None:
             ev[3].record(stream)
-        fa.fa_bwd_postprocess(dq, dk, dv, ws, Hkv, softmax_scale=scale)
+        fa.fa_bwd_dq(q, k, v, do, dq, ws, causal=causal, softmax_scale=scale)
         if ev is not None:
             ev[4].record(stream)
+        fa.fa_bwd_postprocess(dk, dv, ws, Hq)
+        if ev is not None:
+            ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps, bracketed by device synchronisation.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -155,17 +158,20 @@ def main():
     for ev in evs:
         for i, kname in enumerate(kernels):
             per_kernel[kname].append(ev[i].elapsed_time(ev[i + 1]))
-        step_ms.append(ev[0].elapsed_time(ev[4]))
+        step_ms.append(ev[0].elapsed_time(ev[len(kernels)]))
     avg = {kname: statistics.fmean(vals) for kname, vals in per_kernel.items()}
     med = {kname: statistics.median(vals) for kname, vals in per_kernel.items()}
     ms_per_step = wall * 1e3 / args.steps
 
     f_fwd, f_bwd = flops(shape, True, False), flops(shape, False, True)
     fwd_ms = avg["fwd"]
-    bwd_ms = avg["bwd_preprocess"] + avg["bwd_main"] + avg["bwd_postprocess"]
+    bwd_ms = sum(avg[kname] for kname in kernels if kname != "fwd")
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     dominant = max(kernels, key=lambda kname: avg[kname])
-    kflops = {"fwd": f_fwd, "bwd_main": f_bwd, "bwd_preprocess": 0.0, "bwd_postprocess": 0.0}
+    # Algorithmic FLOPs per launch: the dK/dV pass does four of the backward's five N x N x D
+    # products (S, dP, dV, dK); the dQ pass recomputes S and dP and does dQ (three).
+    kflops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.6 * f_bwd,
+              "bwd_preprocess": 0.0, "bwd_postprocess": 0.0}
     if kflops[dominant] > 0:
         achieved = kflops[dominant] / (avg[dominant] * 1e-3) / 1e12
         roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),

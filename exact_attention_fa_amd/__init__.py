@@ -21,7 +21,7 @@ import os
 import threading
 
 __all__ = [
-    "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_postprocess",
+    "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_postprocess",
     "fa_bwd_workspace_size", "fa_version", "fa_status_string", "library_path", "load_library",
     "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16",
 ]
@@ -45,11 +45,14 @@ _SIGS = {
                ctypes.c_int),
     "fa_bwd_preprocess": ([_vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
                            ctypes.c_int, _vp], ctypes.c_int),
-    "fa_bwd_main": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+    "fa_bwd_dkdv": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                      _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
                     ctypes.c_int),
-    "fa_bwd_postprocess": ([_vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
-                            ctypes.c_float, ctypes.c_int, _vp], ctypes.c_int),
+    "fa_bwd_dq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                   _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
+                  ctypes.c_int),
+    "fa_bwd_postprocess": ([_vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
+                            ctypes.c_int, _vp], ctypes.c_int),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -190,20 +193,29 @@ def fa_bwd_preprocess(o, do, lse, workspace, Hkv: int):
     _check(rc, "fa_bwd_preprocess")
 
 
-def fa_bwd_main(q, k, v, do, lse, dk, dv, workspace, causal=False, softmax_scale=None):
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def fa_bwd_dkdv(q, k, v, do, dk, dv, workspace, causal=False, softmax_scale=None):
     B, Hq, Hkv, N, D = _dims(q, k, v)
-    rc = load_library().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk),
-                                    _ptr(dv), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, D,
+    rc = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
+                                    _ptr(workspace), _nbytes(workspace), B, Hq, Hkv, N, D,
                                     _scale(D, softmax_scale), int(bool(causal)), _dtype_code(q),
                                     _stream(q))
-    _check(rc, "fa_bwd_main")
+    _check(rc, "fa_bwd_dkdv")
 
 
-def fa_bwd_postprocess(dq, dk, dv, workspace, Hkv: int, softmax_scale=None):
-    B, Hq, N, D = dq.shape
-    rc = load_library().fa_bwd_postprocess(_ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                                           workspace.numel() * workspace.element_size(),
-                                           B, Hq, Hkv, N, D, _scale(D, softmax_scale),
-                                           _dtype_code(dq), _stream(dq))
+def fa_bwd_dq(q, k, v, do, dq, workspace, causal=False, softmax_scale=None):
+    B, Hq, Hkv, N, D = _dims(q, k, v)
+    rc = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(workspace),
+                                  _nbytes(workspace), B, Hq, Hkv, N, D, _scale(D, softmax_scale),
+                                  int(bool(causal)), _dtype_code(q), _stream(q))
+    _check(rc, "fa_bwd_dq")
+
+
+def fa_bwd_postprocess(dk, dv, workspace, Hq: int):
+    B, Hkv, N, D = dk.shape
+    rc = load_library().fa_bwd_postprocess(_ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
+                                           B, Hq, Hkv, N, D, _dtype_code(dk), _stream(dk))
     _check(rc, "fa_bwd_postprocess")

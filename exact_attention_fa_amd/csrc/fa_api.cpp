@@ -71,8 +71,6 @@ BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long
   BwdWorkspace w{};
   const size_t rows = (size_t)B * (size_t)Hq * (size_t)N;
   size_t off = 0;
-  w.dq_acc = off;
-  off += round_up(rows * (size_t)D * 4);
   w.delta = off;
   off += round_up(rows * 4);
   w.lse2 = off;
@@ -175,7 +173,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const BwdArgs a = make_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, D, softmax_scale,
                                   causal, dtype, stream);
   FA_TRY(status_of(launch_bwd_preprocess(a)));
-  FA_TRY(status_of(launch_bwd_main(a)));
+  FA_TRY(status_of(launch_bwd_dkdv(a)));
+  FA_TRY(status_of(launch_bwd_dq(a)));
   return status_of(launch_bwd_postprocess(a));
 }
 
@@ -194,14 +193,13 @@ int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* w
   return status_of(launch_bwd_preprocess(a));
 }
 
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk, void* dv,
-                void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
                 float softmax_scale, int causal, int dtype, void* stream) {
   FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
   FA_TRY(check_scale(softmax_scale));
   const void* p16[] = {q, k, v, dout};
   for (const void* p : p16) FA_TRY(check_ptr(p, 16));
-  FA_TRY(check_ptr(lse, 4));
   const bool direct = Hq == Hkv;
   if (direct) {
     FA_TRY(check_ptr(dk, 16));
@@ -209,32 +207,41 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, c
   }
   const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
   const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {dout, qb, false},
-                     {lse, (size_t)(B * Hq * N) * 4, false},
                      {direct ? dk : nullptr, kb, true}, {direct ? dv : nullptr, kb, true},
-                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, true}};
-  FA_TRY(check_alias(r, 8));
-  const BwdArgs a = make_bwd_args(q, k, v, nullptr, dout, lse, nullptr, dk, dv, workspace, B, Hq, Hkv, N, D,
+                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, !direct}};
+  FA_TRY(check_alias(r, 7));
+  const BwdArgs a = make_bwd_args(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv, workspace, B, Hq, Hkv, N, D,
                                   softmax_scale, causal, dtype, stream);
-  return status_of(launch_bwd_main(a));
+  return status_of(launch_bwd_dkdv(a));
 }
 
-int fa_bwd_postprocess(void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B,
-                       int64_t Hq, int64_t Hkv, int64_t N, int64_t D, float softmax_scale, int dtype,
-                       void* stream) {
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, void* workspace,
+              size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+              float softmax_scale, int causal, int dtype, void* stream) {
   FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
   FA_TRY(check_scale(softmax_scale));
-  FA_TRY(check_ptr(dq, 16));
-  const bool reduce = Hq != Hkv;
-  if (reduce) {
-    FA_TRY(check_ptr(dk, 16));
-    FA_TRY(check_ptr(dv, 16));
-  }
+  const void* p16[] = {q, k, v, dout, dq};
+  for (const void* p : p16) FA_TRY(check_ptr(p, 16));
   const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
-  const Range r[] = {{dq, qb, true}, {reduce ? dk : nullptr, kb, true}, {reduce ? dv : nullptr, kb, true},
+  const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {dout, qb, false}, {dq, qb, true},
                      {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, false}};
-  FA_TRY(check_alias(r, 4));
-  const BwdArgs a = make_bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, workspace, B,
-                                  Hq, Hkv, N, D, softmax_scale, 0, dtype, stream);
+  FA_TRY(check_alias(r, 6));
+  const BwdArgs a = make_bwd_args(q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, D,
+                                  softmax_scale, causal, dtype, stream);
+  return status_of(launch_bwd_dq(a));
+}
+
+int fa_bwd_postprocess(void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t N, int64_t D, int dtype, void* stream) {
+  FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
+  FA_TRY(check_ptr(dk, 16));
+  FA_TRY(check_ptr(dv, 16));
+  const size_t kb = (size_t)(B * Hkv * N * D) * 2;
+  const Range r[] = {{dk, kb, true}, {dv, kb, true},
+                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, false}};
+  FA_TRY(check_alias(r, 3));
+  const BwdArgs a = make_bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dk, dv, workspace,
+                                  B, Hq, Hkv, N, D, 1.f, 0, dtype, stream);
   return status_of(launch_bwd_postprocess(a));
 }
 

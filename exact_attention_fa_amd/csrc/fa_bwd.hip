@@ -1,27 +1,24 @@
-// Fused exact attention backward for gfx950: preprocess, main, postprocess.
+// Fused exact attention backward for gfx950: preprocess, dK/dV pass, dQ pass, postprocess.
 //
 // The method: P is recomputed from the saved log-sum-exp, then
 //   dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dK = scale * dS^T Q, dQ = scale * dS K
 // with D = rowsum(dO * O).  The score-gradient step is a cancellation, so dP and dS stay
 // in fp32 and only the MFMA operands are rounded to the input type ("FlashAttention for
-// Tesla P100", section "Documentation": the choice of precision is made per product).
-// The page's backward also reads dQ through atomics by default, with a no-atomic variant
-// ("Layout" table); this file uses fp32 atomics into a workspace accumulator.
+// Tesla P100", section "Documentation": the choice of precision is made per product).  That
+// page's backward accumulates dQ with atomics and also ships a no-atomic variant ("Layout"
+// table); here dQ comes from its own query-stationary pass with no atomics, which recomputes
+// S and dP (three products instead of one, but no fp32 atomic traffic, no dS round trip
+// through LDS and a bitwise-deterministic result).
 //
-// gfx950 realisation of the main kernel: a workgroup (4 waves) owns 128 keys of one
-// query head, a wave owns 32 of them.  K and V fragments of those keys stay in registers
-// (and the K tile also in LDS).  64-query tiles of Q and dO, with the per-row LSE*log2(e)
-// and D, stream through double-buffered LDS by direct global->LDS loads issued one tile
-// ahead, so no registers are spent on staging.  Per query tile, per wave and per 32-query
-// block:
-//   S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16 with the key as the accumulator
-//   column, so each lane owns one key; register 8t+j of the block is query 16t + 8g + j
-//   (row permutation of the Q/dO operand).  That register order is exactly the k-slot
-//   order of the A operand of dV += P^T dO and dK += dS^T Q, so the rounded P and dS feed
-//   those MFMAs from registers; the dO and Q B operands come through ds_read_b64_tr_b16.
-//   dS^T is written to LDS; after a barrier the four waves split dQ += dS K of the tile
-//   (both operands read transposed) and add it into the fp32 accumulator with hardware
-//   float atomics.  Barriers wait for LDS traffic only, so the atomics stay in flight.
+// dK/dV pass: a workgroup (4 waves) owns 128 keys of one query head, a wave owns 32 of them;
+// the K and V tiles stay in LDS.  64-query tiles of Q and dO, with the per-row LSE*log2(e)
+// and D, stream through a double-buffered LDS by direct global->LDS loads issued one tile
+// ahead.  Per query tile, per wave and per 32-query block: S = Q K^T and dP = dO V^T on
+// v_mfma_f32_32x32x16 with the key as the accumulator column, so each lane owns one key;
+// register 8t+j of the block is query 16t + 8g + j (row permutation of the Q/dO operand),
+// which is exactly the k-slot order of the A operand of dV += P^T dO and dK += dS^T Q, so
+// the rounded P and dS feed those MFMAs from registers; the dO and Q B operands come through
+// ds_read_b64_tr_b16.
 // Grouped-query attention: the grid runs over query heads; when Hq > Hkv each workgroup
 // writes fp32 per-query-head dK/dV partials that the postprocess sums over the group
 // (deterministic), otherwise it writes dK/dV directly.
@@ -37,15 +34,16 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBwdBKV = 128;  // keys per workgroup (32 per wave)
 constexpr int kBwdBQ = 64;    // query rows per streamed tile
+constexpr int kDqBR = 128;    // dQ kernel: query rows per workgroup (32 per wave)
+constexpr int kDqBC = 64;     // dQ kernel: keys per K/V tile
 
 // ---------------------------------------------------------------- preprocess
-// D[row] = sum_d dO[row][d] * O[row][d] (fp32), L2[row] = LSE[row] * log2(e) (the exponent
-// offset of the base-2 recompute of P) and dQacc[row][:] = 0.
+// D[row] = sum_d dO[row][d] * O[row][d] (fp32) and L2[row] = LSE[row] * log2(e) (the
+// exponent offset of the base-2 recompute of P).
 template <typename TR, int HD>
 __global__ void __launch_bounds__(kThreads)
 bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-               const float* __restrict__ LSE, float* __restrict__ Dl, float* __restrict__ L2,
-               float* __restrict__ dQacc, long long rows) {
+               const float* __restrict__ LSE, float* __restrict__ Dl, float* __restrict__ L2, long long rows) {
   constexpr int TPR = HD / 8;          // threads per row, 8 elements each
   constexpr int RPB = kThreads / TPR;  // rows per block
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -59,9 +57,6 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
       acc = fmaf(TR::lo(o[w]), TR::lo(d[w]), acc);
       acc = fmaf(TR::hi(o[w]), TR::hi(d[w]), acc);
     }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(dQacc + row * HD + part * 8) = z;
-    *reinterpret_cast<f32x4*>(dQacc + row * HD + part * 8 + 4) = z;
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -71,31 +66,28 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
   }
 }
 
-// ---------------------------------------------------------------- main
+// ---------------------------------------------------------------- dK, dV
 template <typename TR, int HD, bool CAUSAL, bool PARTIAL>
 __global__ void __launch_bounds__(kThreads, 1)
-bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                const float* __restrict__ L2, const float* __restrict__ Dl,
-                float* __restrict__ dQacc, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                float* __restrict__ dKp, float* __restrict__ dVp, int Hq, int Hkv, int N, int n_kt,
-                float c2, float scale) {
+                const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
+                uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int Hq, int Hkv,
+                int N, int n_kt, float c2, float scale) {
   constexpr int BKV = kBwdBKV, BQ = kBwdBQ;
   constexpr int KST = HD / 16, DB = HD / 32;
   constexpr int KT_BYTES = BKV * HD * 2;
   constexpr int QT_BYTES = BQ * HD * 2;
-  constexpr int ST_BYTES = BKV * BQ * 2;
   constexpr int KI = KT_BYTES / 1024 / 4;   // 1 KB direct loads per wave for the K tile
   constexpr int QI = QT_BYTES / 1024 / 4;   // ... for one Q (or dO) tile
-  constexpr int NATOM = (DB / 2) * 16;      // dQ atomics a wave issues per query tile
   static_assert(KI * 4096 == KT_BYTES && QI * 4096 == QT_BYTES, "tiles must split into 1 KB loads");
 
-  __shared__ __attribute__((aligned(1024))) char smem[KT_BYTES + 4 * QT_BYTES + ST_BYTES + 4 * BQ * 4];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KT_BYTES + 4 * QT_BYTES + 4 * BQ * 4];
   char* const sK = smem;
-  char* const sQ = sK + KT_BYTES;          // two buffers
+  char* const sV = sK + KT_BYTES;
+  char* const sQ = sV + KT_BYTES;          // two buffers
   char* const sdO = sQ + 2 * QT_BYTES;     // two buffers
-  char* const sdS = sdO + 2 * QT_BYTES;    // dS^T: rows = the workgroup's keys, columns = queries
-  char* const sL = sdS + ST_BYTES;         // two buffers of BQ floats: LSE * log2(e)
+  char* const sL = sdO + 2 * QT_BYTES;     // two buffers of BQ floats: LSE * log2(e)
   char* const sD = sL + 2 * BQ * 4;        // two buffers of BQ floats: D
 
   const int tid = threadIdx.x;
@@ -115,7 +107,6 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* const dOh = dO + (size_t)bh * N * HD;
   const float* const L2h = L2 + (size_t)bh * N;
   const float* const Dh = Dl + (size_t)bh * N;
-  float* const dQh = dQacc + (size_t)bh * N * HD;
 
   const int kv0 = kt * BKV;
   const int kw0 = kv0 + wave * 32;  // this wave's first key
@@ -125,7 +116,7 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // Direct loads of one 64-query tile of Q, dO, L2 and D into buffer `buf`.  Rows past the
   // end read row N-1 (finite data that the masks then zero out).
-  auto issue = [&](int qt, int buf) {
+  auto issue = [&](int qt, char* dQt, char* ddO, char* dL, char* dD) {
     const int q0 = qt * BQ;
 #pragma unroll
     for (int r = 0; r < QI; ++r) {
@@ -133,26 +124,25 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       int row, col;
       sl_pos_to_rc<BQ>((uint32_t)(blk * 64 + lane), row, col);
       const size_t src = (size_t)min(q0 + row, N - 1) * HD + col;
-      dma_to_lds<16>(Qh + src, sQ + buf * QT_BYTES + blk * 1024);
-      dma_to_lds<16>(dOh + src, sdO + buf * QT_BYTES + blk * 1024);
+      dma_to_lds<16>(Qh + src, dQt + blk * 1024);
+      dma_to_lds<16>(dOh + src, ddO + blk * 1024);
     }
-    if (wave == 0) dma_to_lds<4>(L2h + min(q0 + lane, N - 1), sL + buf * BQ * 4);
-    if (wave == 1) dma_to_lds<4>(Dh + min(q0 + lane, N - 1), sD + buf * BQ * 4);
+    if (wave == 0) dma_to_lds<4>(L2h + min(q0 + lane, N - 1), dL);
+    if (wave == 1) dma_to_lds<4>(Dh + min(q0 + lane, N - 1), dD);
   };
 
-  // K tile -> LDS (for dQ += dS K) and the first query tile; V fragments straight into
-  // registers (B operand of dP = dO V^T: slot j of k-step kk = V[key][kk*16 + g*8 + j]).
+  // K and V tiles -> LDS for the whole kernel (keys past the end read key N-1; their scores
+  // are masked), then the first query tile.
 #pragma unroll
   for (int r = 0; r < KI; ++r) {
     const int blk = wave * KI + r;
     int row, col;
     sl_pos_to_rc<BKV>((uint32_t)(blk * 64 + lane), row, col);
-    dma_to_lds<16>(Kh + (size_t)min(kv0 + row, N - 1) * HD + col, sK + blk * 1024);
+    const size_t src = (size_t)min(kv0 + row, N - 1) * HD + col;
+    dma_to_lds<16>(Kh + src, sK + blk * 1024);
+    dma_to_lds<16>(Vh + src, sV + blk * 1024);
   }
-  if (qt0 < n_qt) issue(qt0, 0);
-  u32x4 vr[KST];
-#pragma unroll
-  for (int kk = 0; kk < KST; ++kk) vr[kk] = ld16_if(Vh + (size_t)key * HD + kk * 16 + g * 8, key < N);
+  if (qt0 < n_qt) issue(qt0, sQ, sdO, sL, sD);
 
   // Per-lane LDS offsets (all reads below add compile-time tile offsets to these).
   const uint32_t poff[2] = {sl_off<64>(c, g * 8), sl_off<64>(c, 16 + g * 8)};                   // row c
@@ -161,9 +151,7 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   wait_vmcnt<0>();
   lds_barrier();
-  u32x4 kr[KST];  // B operand of S = Q K^T
-#pragma unroll
-  for (int kk = 0; kk < KST; ++kk) kr[kk] = lds_ld128(sK + sl_off<BKV>(wave * 32, (kk >> 1) * 32) + poff[kk & 1]);
+  // B operands of S = Q K^T and dP = dO V^T for k-step kk: slot j = K/V[key][kk*16 + g*8 + j]
 
   f32x16 dKa[DB], dVa[DB];
 #pragma unroll
@@ -172,39 +160,47 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     dVa[db] = f32x16{};
   }
 
-  // One 64-query tile: recompute S and P, form dP and dS, accumulate dV and dK, and leave
-  // dS^T in LDS for the dQ product.  Register i of the accumulators of query block qb is
+  // One 64-query tile: recompute S and P, form dP and dS, accumulate dV and dK.  Register i of the accumulators of query block qb is
   // query q0 + qb*32 + (i/8)*16 + g*8 + i%8 (permuted Q/dO rows), key `key`; that order is
   // the k-slot order of the A operands of dV = P^T dO and dK = dS^T Q.  The MASKED body
   // handles the causal diagonal and ragged edges; the other one is straight-line code so the
   // two query blocks' MFMAs and softmax work can be interleaved by the scheduler.
   auto tile = [&](auto masked_tag, const int q0, const char* tQ, const char* tdO, const float* tL,
-                  const float* tD) {
+                  const float* tD, const char* tK, const char* tV) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 s[2], dp[2];
+    // ---- S = Q K^T and dP = dO V^T for both query blocks, k-step by k-step
+    struct Ops1 {
+      u32x4 kf, vf, q[2], o[2];
+    };
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    pipelined<KST, 2>(
+        [&](int kk) {
+          Ops1 f;
+          const uint32_t ko = sl_off<BKV>(wave * 32, (kk >> 1) * 32) + poff[kk & 1];
+          f.kf = lds_ld128(tK + ko);
+          f.vf = lds_ld128(tV + ko);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-      if (MASKED && CAUSAL && q0 + qb * 32 + 31 < kw0) continue;  // all above the diagonal
+          for (int qb = 0; qb < 2; ++qb) {
+            const uint32_t o = sl_off<BQ>(qb * 32, (kk >> 1) * 32) + qoff[kk & 1];
+            f.q[qb] = lds_ld128(tQ + o);
+            f.o[qb] = lds_ld128(tdO + o);
+          }
+          return f;
+        },
+        [&](int, const Ops1& f) {
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk)
-        s[qb] = TR::mfma(lds_ld128(tQ + sl_off<BQ>(qb * 32, (kk >> 1) * 32) + qoff[kk & 1]), kr[kk], s[qb]);
-#pragma unroll
-      for (int kk = 0; kk < KST; ++kk)
-        dp[qb] = TR::mfma(lds_ld128(tdO + sl_off<BQ>(qb * 32, (kk >> 1) * 32) + qoff[kk & 1]), vr[kk], dp[qb]);
-    }
+          for (int qb = 0; qb < 2; ++qb) {
+            s[qb] = TR::mfma(f.q[qb], f.kf, s[qb]);
+            dp[qb] = TR::mfma(f.o[qb], f.vf, dp[qb]);
+          }
+        });
+
+    // ---- P = exp2(S c2 - LSE log2 e), dS = P (dP - D); rounded copies are the A operands of
+    //      dV += P^T dO and dK += dS^T Q.
+    u32x4 pa[2][2], dsa[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qb0 = q0 + qb * 32;
-      char* const dsrow = sdS + sl_off<BKV>(wave * 32, qb * 32);
-      if (MASKED && CAUSAL && qb0 + 31 < kw0) {
-        // every key of this wave lies above the diagonal for these 32 queries: dS = 0
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        lds_st128(dsrow + poff[0], z);
-        lds_st128(dsrow + poff[1], z);
-        continue;
-      }
       if (MASKED) {
         // masked scores become -inf, so exp2 (with c2 > 0) makes them exact zeros
 #pragma unroll
@@ -213,7 +209,6 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           if (key >= N || q >= N || (CAUSAL && key > q)) s[qb][i] = -INFINITY;
         }
       }
-      u32x4 pa[2], dsa[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int r0 = qb * 32 + t2 * 16 + g * 8;
@@ -230,69 +225,73 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           p[j] = fast_exp2(fmaf(s[qb][i], c2, -lse2));
           ds[j] = p[j] * (dp[qb][i] - dd);
         }
-        pa[t2] = u32x4{TR::pack(p[0], p[1]), TR::pack(p[2], p[3]), TR::pack(p[4], p[5]), TR::pack(p[6], p[7])};
-        dsa[t2] = u32x4{TR::pack(ds[0], ds[1]), TR::pack(ds[2], ds[3]), TR::pack(ds[4], ds[5]),
-                        TR::pack(ds[6], ds[7])};
-        lds_st128(dsrow + poff[t2], dsa[t2]);
+        pa[qb][t2] = u32x4{TR::pack(p[0], p[1]), TR::pack(p[2], p[3]), TR::pack(p[4], p[5]), TR::pack(p[6], p[7])};
+        dsa[qb][t2] = u32x4{TR::pack(ds[0], ds[1]), TR::pack(ds[2], ds[3]), TR::pack(ds[4], ds[5]),
+                            TR::pack(ds[6], ds[7])};
       }
-      // dV += P^T dO, dK += dS^T Q (the rounded P / dS registers are the A operands)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          dVa[db] = TR::mfma(pa[t2], lds_tr8(tdO + sl_off<BQ>(qb * 32 + t2 * 16, db * 32), trl), dVa[db]);
-          dKa[db] = TR::mfma(dsa[t2], lds_tr8(tQ + sl_off<BQ>(qb * 32 + t2 * 16, db * 32), trl), dKa[db]);
-        }
     }
+
+    // ---- dV += P^T dO, dK += dS^T Q; B operands read transposed from the dO / Q tiles
+    struct Ops2 {
+      u32x4 o, q;
+    };
+    pipelined<2 * DB * 2, 2>(
+        [&](int i) {
+          const int qb = i / (2 * DB), db = (i / 2) % DB, t2 = i % 2;
+          const uint32_t o = sl_off<BQ>(qb * 32 + t2 * 16, db * 32);
+          return Ops2{lds_tr8(tdO + o, trl), lds_tr8(tQ + o, trl)};
+        },
+        [&](int i, const Ops2& f) {
+          const int qb = i / (2 * DB), db = (i / 2) % DB, t2 = i % 2;
+          dVa[db] = TR::mfma(pa[qb][t2], f.o, dVa[db]);
+          dKa[db] = TR::mfma(dsa[qb][t2], f.q, dKa[db]);
+        });
   };
 
-  for (int qt = qt0; qt < n_qt; ++qt) {
+  // One query tile: wait for its loads, prefetch the next, compute.  The LDS buffers are
+  // restrict-qualified parameters so that the compiler can tell this tile's reads from the
+  // direct loads filling the next tile and does not make them wait.
+  auto step = [&](auto masked_tag, const int qt, char* __restrict__ nQ, char* __restrict__ ndO,
+                  char* __restrict__ nL, char* __restrict__ nD, const char* __restrict__ tQ,
+                  const char* __restrict__ tdO, const char* __restrict__ tL, const char* __restrict__ tD,
+                  const char* __restrict__ tK, const char* __restrict__ tV) {
     const int q0 = qt * BQ;
-    const int buf = (qt - qt0) & 1;
     if (qt > qt0) {
-      // This tile's direct loads were issued before the previous tile's NATOM atomics;
-      // vector-memory operations retire in order, so this waits for the loads only.
-      wait_vmcnt<NATOM>();
-      lds_barrier();
+      wait_vmcnt<0>();  // this tile's direct loads (issued one tile ago) have landed
+      lds_barrier();    // ... for every wave; every wave is also done with the previous tile
     }
-    if (qt + 1 < n_qt) issue(qt + 1, buf ^ 1);
+    if (qt + 1 < n_qt) issue(qt + 1, nQ, ndO, nL, nD);
     __builtin_amdgcn_sched_barrier(0);
-    const char* const tQ = sQ + buf * QT_BYTES;
-    const char* const tdO = sdO + buf * QT_BYTES;
-    const float* const tL = reinterpret_cast<const float*>(sL + buf * BQ * 4);
-    const float* const tD = reinterpret_cast<const float*>(sD + buf * BQ * 4);
-    if ((kw0 + 32 > N) || (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31))
-      tile(std::true_type{}, q0, tQ, tdO, tL, tD);
-    else
-      tile(std::false_type{}, q0, tQ, tdO, tL, tD);
+    tile(masked_tag, q0, tQ, tdO, reinterpret_cast<const float*>(tL), reinterpret_cast<const float*>(tD), tK, tV);
+  };
 
-    lds_barrier();  // dS^T of all four waves is in LDS
-
-    // dQ[q0 .. q0+63] += dS K: wave -> 32 queries x HD/2 columns
-    {
-      const int qb = wave & 1;
-#pragma unroll
-      for (int dbi = 0; dbi < DB / 2; ++dbi) {
-        const int db = (wave >> 1) * (DB / 2) + dbi;
-        f32x16 dq = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < BKV / 16; ++ks)
-          dq = TR::mfma(lds_tr8(sdS + sl_off<BKV>(ks * 16, qb * 32), trl),
-                        lds_tr8(sK + sl_off<BKV>(ks * 16, db * 32), trl), dq);
-        float* const dst = dQh + (size_t)(q0 + qb * 32 + g * 4) * HD + db * 32 + c;
-        if (q0 + BQ <= N) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) unsafeAtomicAdd(dst + ((i >> 2) * 8 + (i & 3)) * HD, dq[i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int q = q0 + qb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-            if (q < N) unsafeAtomicAdd(dst + ((i >> 2) * 8 + (i & 3)) * HD, dq[i]);
-          }
-        }
-      }
-    }
+  // Query tiles [qt_a, qt_b) need no mask for any wave of the workgroup (the key tile is
+  // whole, the query tile is whole and lies entirely below the diagonal); the others take
+  // the masked body.  Three single-body loops keep the accumulators in fixed registers.
+  int qt_a = qt0, qt_b = qt0;
+  if (kv0 + BKV <= N) {
+    qt_a = CAUSAL ? min(n_qt, (kv0 + BKV - 1) / BQ + 1) : qt0;  // first tile with q0 >= kv0 + BKV - 1
+    qt_b = max(qt_a, N / BQ);                                   // tiles before the ragged tail
   }
+  char* cQ = sQ;
+  char* cdO = sdO;
+  char* cL = sL;
+  char* cD = sD;
+  char* nQ = sQ + QT_BYTES;
+  char* ndO = sdO + QT_BYTES;
+  char* nL = sL + BQ * 4;
+  char* nD = sD + BQ * 4;
+  auto run = [&](auto masked_tag, int qt) {
+    step(masked_tag, qt, nQ, ndO, nL, nD, cQ, cdO, cL, cD, sK, sV);
+    char* t;
+    t = cQ, cQ = nQ, nQ = t;
+    t = cdO, cdO = ndO, ndO = t;
+    t = cL, cL = nL, nL = t;
+    t = cD, cD = nD, nD = t;
+  };
+  for (int qt = qt0; qt < qt_a; ++qt) run(std::true_type{}, qt);
+  for (int qt = qt_a; qt < qt_b; ++qt) run(std::false_type{}, qt);
+  for (int qt = max(qt_a, qt_b); qt < n_qt; ++qt) run(std::true_type{}, qt);
 
   // ---- epilogue: register i of dKa/dVa[db] <-> key kw0 + (i/4)*8 + g*4 + i%4, column db*32 + c
 #pragma unroll
@@ -314,20 +313,180 @@ bwd_main_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
-// ---------------------------------------------------------------- postprocess
-// dQ = dtype(scale * dQacc), 8 elements per thread.
-template <typename TR>
-__global__ void __launch_bounds__(kThreads)
-bwd_post_dq_kernel(const float* __restrict__ dQacc, uint16_t* __restrict__ dQ, long long n8, float scale) {
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(dQacc + i * 8);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(dQacc + i * 8 + 4);
-  const u32x4 w = {TR::pack(a[0] * scale, a[1] * scale), TR::pack(a[2] * scale, a[3] * scale),
-                   TR::pack(b[0] * scale, b[1] * scale), TR::pack(b[2] * scale, b[3] * scale)};
-  *reinterpret_cast<u32x4*>(dQ + i * 8) = w;
+// ---------------------------------------------------------------- dQ
+// Query-stationary: a workgroup owns 128 query rows (32 per wave) of one head and streams
+// the K/V tiles of its KV head through a double-buffered LDS, exactly like the forward.  Per
+// 64-key tile, per wave:
+//   S^T = K Q^T and dP^T = V dO^T  (K, V rows from LDS; Q and dO fragments in registers)
+//   P^T = exp2(S^T c2 - LSE log2 e),  dS^T = P^T * (dP^T - D)      (fp32, one query per lane)
+//   dQ^T += K^T dS^T  (K^T read transposed from the K tile; the rounded dS^T registers are
+//                      the B operand thanks to the permuted K rows)
+// Every dQ element is produced by exactly one lane: no atomics, bitwise deterministic.
+template <typename TR, int HD, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads, 2)
+bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+              const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
+              int Hq, int Hkv, int N, int n_qt, float c2, float scale) {
+  constexpr int BR = kDqBR, BC = kDqBC;
+  constexpr int KST = HD / 16;              // k-steps over the head dim
+  constexpr int DB = HD / 32;               // 32-row blocks of dQ^T
+  constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
+  constexpr int TI = TILE / 1024 / 4;       // 1 KB direct loads per wave per tile
+  static_assert(TI * 4096 == TILE, "tile must split into 1 KB loads over 4 waves");
+
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2], V[2]
+  char* const sK = smem;
+  char* const sV = smem + 2 * TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, g = lane >> 5;
+
+  const int job = xcd_remap(blockIdx.x, gridDim.x);
+  int qt = job % n_qt;
+  const int bh = job / n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  const int hq = bh % Hq, b = bh / Hq;
+  const int hkv = hq / (Hq / Hkv);
+  const uint16_t* const Kh = K + ((size_t)b * Hkv + hkv) * N * HD;
+  const uint16_t* const Vh = V + ((size_t)b * Hkv + hkv) * N * HD;
+
+  const int qw0 = qt * BR + wave * 32;  // first query row of this wave
+  const int qi = qw0 + c;               // the query of this lane's accumulator column
+
+  int kv_end = (N + BC - 1) / BC;
+  if (CAUSAL) kv_end = (min(N, (qt + 1) * BR) - 1) / BC + 1;
+
+  auto issue = [&](int t, char* dK_, char* dV_) {
+#pragma unroll
+    for (int r = 0; r < TI; ++r) {
+      const int blk = wave * TI + r;
+      int row, col;
+      sl_pos_to_rc<BC>((uint32_t)(blk * 64 + lane), row, col);
+      const size_t src = (size_t)min(t * BC + row, N - 1) * HD + col;
+      dma_to_lds<16>(Kh + src, dK_ + blk * 1024);
+      dma_to_lds<16>(Vh + src, dV_ + blk * 1024);
+    }
+  };
+  issue(0, sK, sV);
+
+  // B operands: slot j of k-step kk = Q[qi][kk*16 + g*8 + j] and dO[qi][...]
+  const size_t rowoff = (size_t)bh * N * HD + (size_t)qi * HD;
+  u32x4 qf[KST], of[KST];
+#pragma unroll
+  for (int kk = 0; kk < KST; ++kk) {
+    qf[kk] = ld16_if(Q + rowoff + kk * 16 + g * 8, qi < N);
+    of[kk] = ld16_if(dO + rowoff + kk * 16 + g * 8, qi < N);
+  }
+  const float l2 = qi < N ? L2[(size_t)bh * N + qi] : 0.f;
+  const float dd = qi < N ? Dl[(size_t)bh * N + qi] : 0.f;
+
+  const uint32_t koff[2] = {sl_off<BC>(perm_rows(c), g * 8), sl_off<BC>(perm_rows(c), 16 + g * 8)};
+  const TrLane trl = tr_lane(lane);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  auto step = [&](const int t, char* __restrict__ nK, char* __restrict__ nV, const char* __restrict__ tK,
+                  const char* __restrict__ tV) {
+    if (t + 1 < kv_end) issue(t + 1, nK, nV);
+    const int kv0 = t * BC;
+    if (CAUSAL && kv0 > qw0 + 31) return;  // tile lies above the diagonal for this wave
+
+    // ---- S^T = K Q^T, dP^T = V dO^T: register i of block kb is key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
+    struct Ops {
+      u32x4 k[2], v[2];
+    };
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    pipelined<KST, 1>(
+        [&](int kk) {
+          Ops f;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const uint32_t o = sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1];
+            f.k[kb] = lds_ld128(tK + o);
+            f.v[kb] = lds_ld128(tV + o);
+          }
+          return f;
+        },
+        [&](int kk, const Ops& f) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = TR::mfma(f.k[kb], qf[kk], s[kb]);
+            dp[kb] = TR::mfma(f.v[kb], of[kk], dp[kb]);
+          }
+        });
+
+    if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0)) {
+      // masked scores become -inf, so exp2 (with c2 > 0) makes them exact zeros
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
+        }
+    }
+
+    // ---- dS^T = P^T (dP^T - D), rounded to the B operand of dQ^T += K^T dS^T
+    u32x4 dsb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        float ds[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = t2 * 8 + j;
+          ds[j] = fast_exp2(fmaf(s[kb][i], c2, -l2)) * (dp[kb][i] - dd);
+        }
+        dsb[kb][t2] = u32x4{TR::pack(ds[0], ds[1]), TR::pack(ds[2], ds[3]), TR::pack(ds[4], ds[5]),
+                            TR::pack(ds[6], ds[7])};
+      }
+
+    // ---- dQ^T += K^T dS^T  (A = K^T: rows d, k = keys, read transposed from the K tile)
+    pipelined<DB * 4, 2>(
+        [&](int i) {
+          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
+          return lds_tr8(tK + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl);
+        },
+        [&](int i, const u32x4& a) {
+          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
+          acc[db] = TR::mfma(a, dsb[kb][t2], acc[db]);
+        });
+  };
+
+  // Unrolled by two so that each half sees fixed buffers (even tiles in buffer 0).
+  for (int t = 0; t < kv_end; t += 2) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    step(t, sK + TILE, sV + TILE, sK, sV);
+    if (t + 1 < kv_end) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      step(t + 1, sK, sV, sK + TILE, sV + TILE);
+    }
+  }
+
+  // ---- epilogue: dQ = scale * acc; register i of acc[db] is column db*32 + (i/4)*8 + g*4 + i%4
+  if (qi < N) {
+    uint16_t* const drow = dQ + rowoff;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = db * 32 + i4 * 8 + g * 4;
+        const u32x2 w = {TR::pack(acc[db][i4 * 4 + 0] * scale, acc[db][i4 * 4 + 1] * scale),
+                         TR::pack(acc[db][i4 * 4 + 2] * scale, acc[db][i4 * 4 + 3] * scale)};
+        *reinterpret_cast<u32x2*>(drow + d) = w;
+      }
+  }
 }
 
+// ---------------------------------------------------------------- postprocess
 // dK/dV of KV head (b, hkv) = sum over its `grp` query heads of the fp32 partials
 // (dK partials already carry the softmax scale).
 template <typename TR>
@@ -362,50 +521,67 @@ hipError_t pre_t(const BwdArgs& a) {
   const long long blocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((bwd_pre_kernel<TR, HD>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse,
-                     reinterpret_cast<float*>(a.ws + w.delta), reinterpret_cast<float*>(a.ws + w.lse2),
-                     reinterpret_cast<float*>(a.ws + w.dq_acc), rows);
+                     reinterpret_cast<float*>(a.ws + w.delta), reinterpret_cast<float*>(a.ws + w.lse2), rows);
   return hipGetLastError();
 }
 
+// c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
+// becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
+inline float exp2_factor(float scale) { return scale > 0.f ? scale * kLog2e : 0x1p-100f; }
+
 template <typename TR, int HD, bool CAUSAL, bool PARTIAL>
-hipError_t main_t(const BwdArgs& a) {
+hipError_t dkdv_t(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
   const int n_kt = (int)((a.N + kBwdBKV - 1) / kBwdBKV);
   const long long blocks = a.B * a.Hq * (long long)n_kt;
   float* const dkp = PARTIAL ? reinterpret_cast<float*>(a.ws + w.dk_part) : nullptr;
   float* const dvp = PARTIAL ? reinterpret_cast<float*>(a.ws + w.dv_part) : nullptr;
-  hipLaunchKernelGGL((bwd_main_kernel<TR, HD, CAUSAL, PARTIAL>), dim3((unsigned)blocks), dim3(kThreads), 0,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<TR, HD, CAUSAL, PARTIAL>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
-                     reinterpret_cast<float*>(a.ws + w.dq_acc),
-                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dkp, dvp, (int)a.Hq,
-                     (int)a.Hkv, (int)a.N, n_kt, a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f, a.scale);
+                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dkp, dvp, (int)a.Hq, (int)a.Hkv,
+                     (int)a.N, n_kt, exp2_factor(a.scale), a.scale);
+  return hipGetLastError();
+}
+
+template <typename TR, int HD>
+hipError_t dkdv_hd(const BwdArgs& a) {
+  const bool partial = a.Hq != a.Hkv;
+  if (a.causal) return partial ? dkdv_t<TR, HD, true, true>(a) : dkdv_t<TR, HD, true, false>(a);
+  return partial ? dkdv_t<TR, HD, false, true>(a) : dkdv_t<TR, HD, false, false>(a);
+}
+
+template <typename TR, int HD, bool CAUSAL>
+hipError_t dq_t(const BwdArgs& a) {
+  const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
+  const int n_qt = (int)((a.N + kDqBR - 1) / kDqBR);
+  const long long blocks = a.B * a.Hq * (long long)n_qt;
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
+                     reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
+                     static_cast<uint16_t*>(a.dq), (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, exp2_factor(a.scale),
+                     a.scale);
   return hipGetLastError();
 }
 
 template <typename TR>
+hipError_t dq_dt(const BwdArgs& a) {
+  if (a.D == 64) return a.causal ? dq_t<TR, 64, true>(a) : dq_t<TR, 64, false>(a);
+  return a.causal ? dq_t<TR, 128, true>(a) : dq_t<TR, 128, false>(a);
+}
+
+template <typename TR>
 hipError_t post_t(const BwdArgs& a) {
+  if (a.Hq == a.Hkv) return hipSuccess;  // dK and dV were written directly
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
-  const long long n8 = a.B * a.Hq * a.N * a.D / 8;
-  hipLaunchKernelGGL((bwd_post_dq_kernel<TR>), dim3((unsigned)((n8 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     a.stream, reinterpret_cast<const float*>(a.ws + w.dq_acc), static_cast<uint16_t*>(a.dq), n8,
-                     a.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.Hq == a.Hkv) return e;
   const long long kv8 = a.B * a.Hkv * a.N * a.D / 8;
   hipLaunchKernelGGL((bwd_post_dkdv_kernel<TR>), dim3((unsigned)((kv8 + kThreads - 1) / kThreads)), dim3(kThreads),
                      0, a.stream, reinterpret_cast<const float*>(a.ws + w.dk_part),
                      reinterpret_cast<const float*>(a.ws + w.dv_part), static_cast<uint16_t*>(a.dk),
                      static_cast<uint16_t*>(a.dv), (int)(a.Hq / a.Hkv), a.N * a.D / 8, kv8);
   return hipGetLastError();
-}
-
-template <typename TR, int HD>
-hipError_t main_hd(const BwdArgs& a) {
-  const bool partial = a.Hq != a.Hkv;
-  if (a.causal) return partial ? main_t<TR, HD, true, true>(a) : main_t<TR, HD, true, false>(a);
-  return partial ? main_t<TR, HD, false, true>(a) : main_t<TR, HD, false, false>(a);
 }
 
 }  // namespace
@@ -415,10 +591,12 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a) {
   return a.D == 64 ? pre_t<F16, 64>(a) : pre_t<F16, 128>(a);
 }
 
-hipError_t launch_bwd_main(const BwdArgs& a) {
-  if (a.bf16) return a.D == 64 ? main_hd<Bf16, 64>(a) : main_hd<Bf16, 128>(a);
-  return a.D == 64 ? main_hd<F16, 64>(a) : main_hd<F16, 128>(a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+  if (a.bf16) return a.D == 64 ? dkdv_hd<Bf16, 64>(a) : dkdv_hd<Bf16, 128>(a);
+  return a.D == 64 ? dkdv_hd<F16, 64>(a) : dkdv_hd<F16, 128>(a);
 }
+
+hipError_t launch_bwd_dq(const BwdArgs& a) { return a.bf16 ? dq_dt<Bf16>(a) : dq_dt<F16>(a); }
 
 hipError_t launch_bwd_postprocess(const BwdArgs& a) {
   return a.bf16 ? post_t<Bf16>(a) : post_t<F16>(a);

@@ -178,6 +178,27 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- software pipelining
+
+// Runs compute(i, operands_i) for i = 0..NSTEP-1 with the LDS reads of step i + DIST issued
+// before step i computes (a register ring of DIST + 1 operand sets).  The fences pin this
+// order, so the waits the compiler inserts are partial (LDS reads retire in order) and a
+// wave keeps DIST steps of reads in flight behind its MFMAs.
+template <int NSTEP, int DIST, typename LoadF, typename ComputeF>
+__device__ __forceinline__ void pipelined(LoadF&& load, ComputeF&& compute) {
+  using Ops = decltype(load(0));
+  Ops ring[DIST + 1];
+#pragma unroll
+  for (int i = 0; i < DIST && i < NSTEP; ++i) ring[i] = load(i);
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    if (i + DIST < NSTEP) ring[(i + DIST) % (DIST + 1)] = load(i + DIST);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(i, ring[i % (DIST + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------- synchronisation
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations only.  (HIP's
@@ -186,6 +207,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup barrier that drains only this wave's LDS operations, even while direct
+// global->LDS loads are still in flight (lds_barrier's fence would also wait for those,
+// since they write LDS).  For hand-offs of LDS data written with ordinary LDS stores; the
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_store_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // s_waitcnt vmcnt(N): wait until at most N of this wave's vector-memory operations are

@@ -71,18 +71,18 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // Direct loads of K/V tile t into buffer `buf`; keys past the end read key N-1 (finite
   // data that the masks then exclude).
-  auto issue = [&](int t, int buf) {
+  auto issue = [&](int t, char* dK, char* dV) {
 #pragma unroll
     for (int r = 0; r < TI; ++r) {
       const int blk = wave * TI + r;
       int row, col;
       sl_pos_to_rc<BC>((uint32_t)(blk * 64 + lane), row, col);
       const size_t src = (size_t)min(t * BC + row, N - 1) * HD + col;
-      dma_to_lds<16>(Kh + src, sK + buf * TILE + blk * 1024);
-      dma_to_lds<16>(Vh + src, sV + buf * TILE + blk * 1024);
+      dma_to_lds<16>(Kh + src, dK + blk * 1024);
+      dma_to_lds<16>(Vh + src, dV + blk * 1024);
     }
   };
-  issue(0, 0);
+  issue(0, sK, sV);
 
   // Q fragments: B operand of S^T = K Q^T (slot j of k-step kk = Q[qi][kk*16 + g*8 + j]).
   u32x4 qf[KST];
@@ -100,15 +100,15 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m_run = -INFINITY;  // running (reference) max of raw scores for query qi
   float l_run = 0.f;        // this lane's share of the running sum of 2^((s - m) * c2)
 
-  for (int t = 0; t < kv_end; ++t) {
-    wait_vmcnt<0>();  // this wave's share of tile t has landed
-    lds_barrier();    // ... and everyone's; everyone is also done with tile t-1
-    if (t + 1 < kv_end) issue(t + 1, (t + 1) & 1);
+  // One K/V tile.  The LDS buffers are restrict-qualified parameters so that the compiler
+  // can tell the reads of tile t from the direct loads filling tile t+1 and does not make
+  // the reads wait for those loads.
+  auto step = [&](const int t, char* __restrict__ nK, char* __restrict__ nV, const char* __restrict__ tK,
+                  const char* __restrict__ tV) {
+    if (t + 1 < kv_end) issue(t + 1, nK, nV);
 
     const int kv0 = t * BC;
-    if (CAUSAL && kv0 > qw0 + 31) continue;  // tile lies above the diagonal for this wave
-    const char* const tK = sK + (t & 1) * TILE;
-    const char* const tV = sV + (t & 1) * TILE;
+    if (CAUSAL && kv0 > qw0 + 31) return;  // tile lies above the diagonal for this wave
 
     // ---- S^T = K Q^T: register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
     f32x16 s[2];
@@ -182,6 +182,18 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
           acc[db] = TR::mfma(lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl), pb[kb][t2], acc[db]);
+  };
+
+  // Unrolled by two so that each half sees fixed buffers (even tiles in buffer 0).
+  for (int t = 0; t < kv_end; t += 2) {
+    wait_vmcnt<0>();  // this wave's share of tile t has landed
+    lds_barrier();    // ... and everyone's; everyone is also done with tile t-1
+    step(t, sK + TILE, sV + TILE, sK, sV);
+    if (t + 1 < kv_end) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      step(t + 1, sK, sV, sK + TILE, sV + TILE);
+    }
   }
 
   // ---- epilogue: normalise, write O (input dtype, RNE) and LSE (natural log, fp32)

@@ -23,7 +23,6 @@ struct FwdArgs {
 
 // Workspace carve-up used by the backward stages (byte offsets from the base).
 struct BwdWorkspace {
-  size_t dq_acc;   // fp32 (B, Hq, N, D): dQ accumulated over K/V tiles
   size_t delta;    // fp32 (B, Hq, N): D = rowsum(dO * O)
   size_t lse2;     // fp32 (B, Hq, N): LSE * log2(e)
   size_t dk_part;  // fp32 (B, Hq, N, D): per-query-head dK partials (only when Hq > Hkv)
@@ -52,7 +51,8 @@ struct BwdArgs {
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
-hipError_t launch_bwd_main(const BwdArgs& a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_postprocess(const BwdArgs& a);
 
 }  // namespace fa

@@ -90,8 +90,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            float softmax_scale, int causal, int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs (fp32 dQ accumulator, the D and LSE*log2(e)
- * vectors and, when Hq > Hkv, per-query-head dK/dV partials).  Returns 0 for invalid shapes.
+ * Bytes of device workspace fa_bwd needs: the fp32 D = rowsum(dO * O) and LSE * log2(e)
+ * vectors and, when Hq > Hkv, fp32 per-query-head dK/dV partials.  Returns 0 for invalid
+ * shapes.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D);
 
@@ -100,8 +101,8 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
  * outputs dq (shape of q), dk and dv (shape of k); all 16-bit tensors in `dtype`.
  * workspace: caller-owned device memory of at least fa_bwd_workspace_size(...) bytes,
  * contents undefined before and after.  Enqueues, in order, fa_bwd_preprocess,
- * fa_bwd_main and fa_bwd_postprocess.  dK and dV are deterministic; dQ is accumulated
- * with fp32 atomics, so its last bits may vary from run to run.
+ * fa_bwd_dkdv, fa_bwd_dq and fa_bwd_postprocess.  No atomics: every output element is
+ * reduced in a fixed order, so the result is bitwise deterministic.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -109,29 +110,31 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            float softmax_scale, int causal, int dtype, void* stream);
 
 /*
- * The three stages of fa_bwd, exported so a caller (or a profiler harness) can place
- * events between them.  Running them in this order on one stream with the same
- * workspace is exactly fa_bwd.
- *   fa_bwd_preprocess:  D = rowsum(dout * o) and LSE * log2(e) into the workspace (fp32);
- *                       zeroes the dQ accumulator.
- *   fa_bwd_main:        recomputes P from the workspace's LSE * log2(e), adds scale-free
- *                       dS K into the dQ accumulator, and writes dk/dv (Hq == Hkv) or fp32
- *                       per-query-head partials into the workspace (Hq > Hkv).  Needs the
- *                       preprocess results; its lse argument is only validated.
- *   fa_bwd_postprocess: dq = scale * accumulator in `dtype`; for Hq > Hkv also sums the
- *                       dK/dV partials over each group into dk/dv.
- * Arguments a stage does not use may be NULL (and are then not checked).
+ * The stages of fa_bwd, exported so a caller (or a profiler harness) can place events
+ * between them.  Running them in this order on one stream with the same workspace is
+ * exactly fa_bwd (fa_bwd_dkdv and fa_bwd_dq only depend on the preprocess and may run in
+ * either order).
+ *   fa_bwd_preprocess:  D = rowsum(dout * o) and LSE * log2(e) into the workspace (fp32).
+ *   fa_bwd_dkdv:        key-stationary pass: recomputes P from the workspace's LSE and
+ *                       writes dk = scale * dS^T Q and dv = P^T dO (Hq == Hkv), or fp32
+ *                       per-query-head partials into the workspace (Hq > Hkv).
+ *   fa_bwd_dq:          query-stationary pass: recomputes P and dS and writes
+ *                       dq = scale * dS K.
+ *   fa_bwd_postprocess: for Hq > Hkv, sums the dK/dV partials over each query-head group into
+ *                       dk/dv; for Hq == Hkv it enqueues nothing.
  */
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
                       size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
                       int dtype, void* stream);
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
-                float softmax_scale, int causal, int dtype, void* stream);
-int fa_bwd_postprocess(void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
-                       float softmax_scale, int dtype, void* stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                int64_t D, float softmax_scale, int causal, int dtype, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+              void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+              int64_t D, float softmax_scale, int causal, int dtype, void* stream);
+int fa_bwd_postprocess(void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
+                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -103,7 +103,7 @@ def test_workspace_size(lib):
     B, Hq, Hkv, N, D = 1, 16, 4, 4000, 128
     up = lambda x: (x + 255) // 256 * 256
     rows = B * Hq * N
-    mha = up(rows * D * 4) + 2 * up(rows * 4)
+    mha = 2 * up(rows * 4)
     assert fa.fa_bwd_workspace_size(B, Hq, Hq, N, D) == mha
     assert fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D) == mha + 2 * up(rows * D * 4)
     assert fa.fa_bwd_workspace_size(0, Hq, Hkv, N, D) == 0
@@ -141,15 +141,21 @@ def test_stage_entry_points_reject(lib):
         STATUS["FA_ERR_NULL_POINTER"]
     assert lib.fa_bwd_preprocess(ptr(0), ptr(1), ctypes.c_void_p(A + 2), ptr(2), need, B, Hq, Hkv, N, D, 1,
                                  None) == STATUS["FA_ERR_ALIGNMENT"]
-    assert lib.fa_bwd_main(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), None, None, ptr(5), need,
+    assert lib.fa_bwd_dkdv(ptr(0), ptr(1), ptr(2), ptr(3), None, None, ptr(5), need,
                            B, Hq, Hkv, N, 32, 0.1, 1, 1, None) == STATUS["FA_ERR_HEAD_DIM"]
-    # MHA needs dk/dv pointers in the main stage; GQA needs them in the postprocess
-    assert lib.fa_bwd_main(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), None, None, ptr(5),
+    # MHA writes dk/dv in the dK/dV stage; GQA writes them in the postprocess
+    assert lib.fa_bwd_dkdv(ptr(0), ptr(1), ptr(2), ptr(3), None, None, ptr(5),
                            fa.fa_bwd_workspace_size(B, 2, 2, N, D), B, 2, 2, N, D, 0.1, 1, 1,
                            None) == STATUS["FA_ERR_NULL_POINTER"]
-    assert lib.fa_bwd_postprocess(ptr(0), None, None, ptr(5), need, B, Hq, Hkv, N, D, 0.1, 1, None) == \
+    assert lib.fa_bwd_dq(ptr(0), ptr(1), ptr(2), ptr(3), None, ptr(5), need, B, Hq, Hkv, N, D, 0.1, 1, 1,
+                         None) == STATUS["FA_ERR_NULL_POINTER"]
+    assert lib.fa_bwd_dq(ptr(0), ptr(1), ptr(2), ptr(3), ptr(0), ptr(5), need, B, Hq, Hkv, N, D, 0.1, 1, 1,
+                         None) == STATUS["FA_ERR_ALIAS"]
+    assert lib.fa_bwd_dq(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), need, B, Hq, Hkv, N, D, -0.1, 1, 1,
+                         None) == STATUS["FA_ERR_SCALE"]
+    assert lib.fa_bwd_postprocess(None, ptr(2), ptr(5), need, B, Hq, Hkv, N, D, 1, None) == \
         STATUS["FA_ERR_NULL_POINTER"]
-    assert lib.fa_bwd_postprocess(ptr(0), ptr(1), ptr(2), ptr(0), need, B, Hq, Hkv, N, D, 0.1, 1, None) == \
+    assert lib.fa_bwd_postprocess(ptr(1), ptr(2), ptr(1), need, B, Hq, Hkv, N, D, 1, None) == \
         STATUS["FA_ERR_ALIAS"]
 
 
