@@ -111,14 +111,20 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (CAUSAL && kv0 > qw0 + 31) return;  // tile lies above the diagonal for this wave
 
     // ---- S^T = K Q^T: register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
-    f32x16 s[2];
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    pipelined<KST, 2>(
+        [&](int kk) {
+          struct {
+            u32x4 k[2];
+          } f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+          for (int kb = 0; kb < 2; ++kb) f.k[kb] = lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]);
+          return f;
+        },
+        [&](int kk, const auto& f) {
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk)
-        s[kb] = TR::mfma(lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]), qf[kk], s[kb]);
-    }
+          for (int kb = 0; kb < 2; ++kb) s[kb] = TR::mfma(f.k[kb], qf[kk], s[kb]);
+        });
 
     // ---- masks only on the ragged last tile and tiles crossing the diagonal (a uniform
     //      branch): masked scores become -inf, so exp2 (with c2 > 0) makes exact zeros.
@@ -175,13 +181,15 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
 
     // ---- O^T += V^T P^T  (A = V^T: rows d, k = keys, read transposed from the V tile)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-          acc[db] = TR::mfma(lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl), pb[kb][t2], acc[db]);
+    pipelined<DB * 4, 2>(
+        [&](int i) {
+          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
+          return lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl);
+        },
+        [&](int i, const u32x4& a) {
+          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
+          acc[db] = TR::mfma(a, pb[kb][t2], acc[db]);
+        });
   };
 
   // Unrolled by two so that each half sees fixed buffers (even tiles in buffer 0).

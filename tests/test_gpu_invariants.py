@@ -151,3 +151,35 @@ def test_no_drift_along_sequence(torch_fa):
     bins = err.reshape(8, -1).max(axis=1)
     log("per-bin max error", bins)
     assert bins[-1] <= 2 * bins[0] + 2e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_bitwise_deterministic(torch_fa, causal):
+    """No atomics anywhere in the backward: repeated runs give identical bits."""
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    q, k, v, do = inputs(Shape(1, 8, 2, 1300, 128, "bf16", causal), 21)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    g1 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    g2 = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_stages_equal_fused_call(torch_fa):
+    """The exported stages, run in order on one stream, reproduce fa_bwd bit for bit."""
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    shape = Shape(2, 8, 4, 700, 64, "fp16", True)
+    q, k, v, do = inputs(shape, 23)
+    o, lse = fa.fa_fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=True)
+    ws = torch.empty(fa.fa_bwd_workspace_size(2, 8, 4, 700, 64), dtype=torch.uint8, device="cuda")
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    fa.fa_bwd_preprocess(o, do, lse, ws, 4)
+    fa.fa_bwd_dkdv(q, k, v, do, dk2, dv2, ws, causal=True)
+    fa.fa_bwd_dq(q, k, v, do, dq2, ws, causal=True)
+    fa.fa_bwd_postprocess(dk2, dv2, ws, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
