@@ -115,32 +115,42 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int qt0 = CAUSAL ? kv0 / BQ : 0;  // earlier query tiles see none of these keys
 
   // Direct loads of one 64-query tile of Q, dO, L2 and D into buffer `buf`.  Rows past the
-  // end read row N-1 (finite data that the masks then zero out).
+  // end read as zero (their scores are masked).
+  const uint32_t rowb = (uint32_t)N * HD * 2u;
+  const BufRes rQ = make_bufres(Qh, rowb), rdO = make_bufres(dOh, rowb);
+  const BufRes rL = make_bufres(L2h, (uint32_t)N * 4u), rD = make_bufres(Dh, (uint32_t)N * 4u);
+  uint32_t qvo[QI];
+#pragma unroll
+  for (int r = 0; r < QI; ++r) {
+    int row, col;
+    sl_pos_to_rc<BQ>((uint32_t)((wave * QI + r) * 64 + lane), row, col);
+    qvo[r] = (uint32_t)(row * HD + col) * 2u;
+  }
   auto issue = [&](int qt, char* dQt, char* ddO, char* dL, char* dD) {
-    const int q0 = qt * BQ;
+    const uint32_t q0 = (uint32_t)qt * BQ;
 #pragma unroll
     for (int r = 0; r < QI; ++r) {
       const int blk = wave * QI + r;
-      int row, col;
-      sl_pos_to_rc<BQ>((uint32_t)(blk * 64 + lane), row, col);
-      const size_t src = (size_t)min(q0 + row, N - 1) * HD + col;
-      dma_to_lds<16>(Qh + src, dQt + blk * 1024);
-      dma_to_lds<16>(dOh + src, ddO + blk * 1024);
+      dma_to_lds<16>(rQ, qvo[r], q0 * (HD * 2), dQt + blk * 1024);
+      dma_to_lds<16>(rdO, qvo[r], q0 * (HD * 2), ddO + blk * 1024);
     }
-    if (wave == 0) dma_to_lds<4>(L2h + min(q0 + lane, N - 1), dL);
-    if (wave == 1) dma_to_lds<4>(Dh + min(q0 + lane, N - 1), dD);
+    if (wave == 0) dma_to_lds<4>(rL, (uint32_t)lane * 4u, q0 * 4u, dL);
+    if (wave == 1) dma_to_lds<4>(rD, (uint32_t)lane * 4u, q0 * 4u, dD);
   };
 
-  // K and V tiles -> LDS for the whole kernel (keys past the end read key N-1; their scores
+  // K and V tiles -> LDS for the whole kernel (keys past the end read as zero; their scores
   // are masked), then the first query tile.
+  {
+    const BufRes rK = make_bufres(Kh, rowb), rV = make_bufres(Vh, rowb);
 #pragma unroll
-  for (int r = 0; r < KI; ++r) {
-    const int blk = wave * KI + r;
-    int row, col;
-    sl_pos_to_rc<BKV>((uint32_t)(blk * 64 + lane), row, col);
-    const size_t src = (size_t)min(kv0 + row, N - 1) * HD + col;
-    dma_to_lds<16>(Kh + src, sK + blk * 1024);
-    dma_to_lds<16>(Vh + src, sV + blk * 1024);
+    for (int r = 0; r < KI; ++r) {
+      const int blk = wave * KI + r;
+      int row, col;
+      sl_pos_to_rc<BKV>((uint32_t)(blk * 64 + lane), row, col);
+      const uint32_t vo = (uint32_t)(row * HD + col) * 2u;
+      dma_to_lds<16>(rK, vo, (uint32_t)kv0 * (HD * 2), sK + blk * 1024);
+      dma_to_lds<16>(rV, vo, (uint32_t)kv0 * (HD * 2), sV + blk * 1024);
+    }
   }
   if (qt0 < n_qt) issue(qt0, sQ, sdO, sL, sD);
 
@@ -359,15 +369,21 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int kv_end = (N + BC - 1) / BC;
   if (CAUSAL) kv_end = (min(N, (qt + 1) * BR) - 1) / BC + 1;
 
+  // Direct loads of K/V tile t (keys past the end read as zero; their scores are masked).
+  const BufRes rK = make_bufres(Kh, (uint32_t)N * HD * 2u), rV = make_bufres(Vh, (uint32_t)N * HD * 2u);
+  uint32_t kvo[TI];
+#pragma unroll
+  for (int r = 0; r < TI; ++r) {
+    int row, col;
+    sl_pos_to_rc<BC>((uint32_t)((wave * TI + r) * 64 + lane), row, col);
+    kvo[r] = (uint32_t)(row * HD + col) * 2u;
+  }
   auto issue = [&](int t, char* dK_, char* dV_) {
 #pragma unroll
     for (int r = 0; r < TI; ++r) {
       const int blk = wave * TI + r;
-      int row, col;
-      sl_pos_to_rc<BC>((uint32_t)(blk * 64 + lane), row, col);
-      const size_t src = (size_t)min(t * BC + row, N - 1) * HD + col;
-      dma_to_lds<16>(Kh + src, dK_ + blk * 1024);
-      dma_to_lds<16>(Vh + src, dV_ + blk * 1024);
+      dma_to_lds<16>(rK, kvo[r], (uint32_t)t * (BC * HD * 2), dK_ + blk * 1024);
+      dma_to_lds<16>(rV, kvo[r], (uint32_t)t * (BC * HD * 2), dV_ + blk * 1024);
     }
   };
   issue(0, sK, sV);

@@ -112,17 +112,26 @@ __device__ __forceinline__ void sl_pos_to_rc(uint32_t P, int& row, int& col) {
   col = (int)(slice * 32u + ((pc ^ ((r >> 2) & 3u)) << 3));
 }
 
-// Direct global -> LDS copy (global_load_lds_dwordx4 / _dword): every active lane fetches
-// BYTES from its own address `src`; lane l's data lands at lds_base + BYTES * l.  Completion
-// is tracked by vmcnt.
+// Direct global -> LDS copies go through a buffer resource (buffer_load_dword{,x4} ... lds):
+// every active lane fetches BYTES from base + voff + soff and lane l's data lands at
+// lds_base + BYTES * l.  Completion is tracked by vmcnt only.  Bytes at or past
+// `bytes` (the resource's extent) read as zero, so ragged tails need no clamping.  (The
+// global_load_lds form would do the same copy, but the compiler treats it as a flat access
+// that may touch LDS and then makes every later LDS-read wait drain all outstanding LDS
+// reads, which defeats operand prefetching while a copy is in flight.)
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ __forceinline__ BufRes make_bufres(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw (untyped) 32-bit data, the gfx9-family default for loads.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 template <int BYTES>
-__device__ __forceinline__ void dma_to_lds(const void* src, char* lds_base) {
+__device__ __forceinline__ void dma_to_lds(BufRes res, uint32_t voff, uint32_t soff, char* lds_base) {
   static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte direct loads");
   auto* dst = (__attribute__((address_space(3))) void*)lds_base;
   if constexpr (BYTES == 16)
-    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, dst, 16, voff, soff, 0, 0);
   else
-    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, dst, 4, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 lds_ld128(const char* p) { return *reinterpret_cast<const u32x4*>(p); }

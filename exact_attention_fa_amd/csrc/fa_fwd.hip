@@ -23,6 +23,8 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <type_traits>
+
 namespace fa {
 
 namespace {
@@ -31,6 +33,20 @@ constexpr int kFwdBR = 128;  // query rows per workgroup
 constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kThreads = 256;
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 of the largest probability)
+
+// Work units of the softmax of one tile, in dependency order, spread over the MFMA steps
+// of the P V product they run under: 16 three-way maxima (weight 1 each), the cross-lane
+// reduction and reference update (weight 4), 32 fused scale-subtract + exp2 (weight 3 each).
+constexpr int kSmMax = 16, kSmRed = 16, kSmExp0 = 17, kSmUnits = 49;
+constexpr int sm_weight(int u) { return u < kSmMax ? 1 : (u == kSmRed ? 4 : 3); }
+constexpr int sm_step(int u, int nsteps) {
+  int before = 0, total = 0;
+  for (int v = 0; v < kSmUnits; ++v) {
+    if (v < u) before += sm_weight(v);
+    total += sm_weight(v);
+  }
+  return before * nsteps / total;  // the step in whose share the unit starts
+}
 
 template <typename TR, int HD, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -66,23 +82,29 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int qw0 = qt * BR + wave * 32;  // first query row of this wave
   const int qi = qw0 + c;               // the query row this lane's column belongs to
 
-  int kv_end = (N + BC - 1) / BC;
-  if (CAUSAL) kv_end = (min(N, (qt + 1) * BR) - 1) / BC + 1;
+  // K/V tiles the workgroup streams, and the prefix of them this wave computes on (causal
+  // waves stop at their own diagonal; waves wholly past the last row compute nothing).
+  int T = (N + BC - 1) / BC;
+  if (CAUSAL) T = (min(N, (qt + 1) * BR) - 1) / BC + 1;
+  int Tw = T;
+  if (CAUSAL) Tw = (min(N, qw0 + 32) - 1) / BC + 1;
+  if (qw0 >= N) Tw = 0;
 
-  // Direct loads of K/V tile t into buffer `buf`; keys past the end read key N-1 (finite
-  // data that the masks then exclude).
-  auto issue = [&](int t, char* dK, char* dV) {
+  // Direct loads of tile t of K or V into `dst` (rows past the end read as zero, which the
+  // masks then exclude).
+  const BufRes rK = make_bufres(Kh, (uint32_t)N * HD * 2u), rV = make_bufres(Vh, (uint32_t)N * HD * 2u);
+  uint32_t doff[TI];
 #pragma unroll
-    for (int r = 0; r < TI; ++r) {
-      const int blk = wave * TI + r;
-      int row, col;
-      sl_pos_to_rc<BC>((uint32_t)(blk * 64 + lane), row, col);
-      const size_t src = (size_t)min(t * BC + row, N - 1) * HD + col;
-      dma_to_lds<16>(Kh + src, dK + blk * 1024);
-      dma_to_lds<16>(Vh + src, dV + blk * 1024);
-    }
+  for (int r = 0; r < TI; ++r) {
+    int row, col;
+    sl_pos_to_rc<BC>((uint32_t)((wave * TI + r) * 64 + lane), row, col);
+    doff[r] = (uint32_t)(row * HD + col) * 2u;
+  }
+  auto issue = [&](BufRes res, int t, char* dst) {
+#pragma unroll
+    for (int r = 0; r < TI; ++r) dma_to_lds<16>(res, doff[r], (uint32_t)t * (BC * HD * 2), dst + (wave * TI + r) * 1024);
   };
-  issue(0, sK, sV);
+  issue(rK, 0, sK);
 
   // Q fragments: B operand of S^T = K Q^T (slot j of k-step kk = Q[qi][kk*16 + g*8 + j]).
   u32x4 qf[KST];
@@ -99,109 +121,200 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY;  // running (reference) max of raw scores for query qi
   float l_run = 0.f;        // this lane's share of the running sum of 2^((s - m) * c2)
+  f32x16 p[2];              // probabilities of the previous tile, waiting for P V
 
-  // One K/V tile.  The LDS buffers are restrict-qualified parameters so that the compiler
-  // can tell the reads of tile t from the direct loads filling tile t+1 and does not make
-  // the reads wait for those loads.
-  auto step = [&](const int t, char* __restrict__ nK, char* __restrict__ nV, const char* __restrict__ tK,
-                  const char* __restrict__ tV) {
-    if (t + 1 < kv_end) issue(t + 1, nK, nV);
-
-    const int kv0 = t * BC;
-    if (CAUSAL && kv0 > qw0 + 31) return;  // tile lies above the diagonal for this wave
-
-    // ---- S^T = K Q^T: register i of block kb holds key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    pipelined<KST, 2>(
-        [&](int kk) {
-          struct {
-            u32x4 k[2];
-          } f;
+  // ---- the pieces of one pipeline step; step j computes S_j and its softmax while the
+  //      MFMAs of P_{j-1} V_{j-1} run, so the exp2 work hides under matrix work.  Each MFMA
+  //      step is fenced together with the LDS read of the operand RD steps ahead and a fixed
+  //      share of the VALU work, so the two pipes stay interleaved.
+  constexpr int RD = 4;
+  // K fragment of S-step i (i = kk*2 + kb): key rows kb*32.., head-dim k-step kk.
+  auto kfrag = [&](const char* tK, int i) {
+    const int kk = i >> 1, kb = i & 1;
+    return lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]);
+  };
+  // V^T fragment of PV-step i (i = db*4 + kb*2 + t2).
+  auto vfrag = [&](const char* tV, int i) {
+    const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
+    return lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl);
+  };
+  // S^T_j = K_j Q^T (register i of block kb holds key j*BC + kb*32 + (i/8)*16 + g*8 + i%8),
+  // with valu(i) run under S-step i.
+  auto scores = [&](const char* __restrict__ tK, f32x16 (&s)[2], auto&& valu) {
+    constexpr int NS = 2 * KST;
+    u32x4 ring[RD + 1];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) f.k[kb] = lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]);
-          return f;
-        },
-        [&](int kk, const auto& f) {
+    for (int i = 0; i < RD; ++i) ring[i] = kfrag(tK, i);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) s[kb] = TR::mfma(f.k[kb], qf[kk], s[kb]);
-        });
-
-    // ---- masks only on the ragged last tile and tiles crossing the diagonal (a uniform
-    //      branch): masked scores become -inf, so exp2 (with c2 > 0) makes exact zeros.
-    if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0)) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-          if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
-        }
+    for (int i = 0; i < NS; ++i) {
+      if (i + RD < NS) ring[(i + RD) % (RD + 1)] = kfrag(tK, i + RD);
+      __builtin_amdgcn_sched_barrier(0);
+      s[i & 1] = TR::mfma(ring[i % (RD + 1)], qf[i >> 1], s[i & 1]);
+      valu(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // ---- online softmax in raw-score units (c2 = scale * log2(e) > 0).  The reference max
-    //      moves only when the tile max exceeds it by more than 2^kRescaleLog2 in the exp2
-    //      domain (always on the first tile); otherwise probabilities up to 2^kRescaleLog2
-    //      accumulate against the stale reference, exact because O and l share it.
-    float mx = s[0][0];
+  };
+  // O^T += V^T P^T (A = V^T: rows d, k = keys, read transposed from the V tile), with
+  // valu(i) run under PV-step i.
+  auto pv = [&](const char* __restrict__ tV, const u32x4 (&pb)[2][2], auto&& valu) {
+    constexpr int NS = DB * 4;
+    u32x4 ring[RD + 1];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < RD; ++i) ring[i] = vfrag(tV, i);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);  // finite: key 0 of tile 0 is visible to every row
-    const bool grow = (m_run == -INFINITY) || ((m_new - m_run) * c2 > kRescaleLog2);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c2);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    for (int i = 0; i < NS; ++i) {
+      if (i + RD < NS) ring[(i + RD) % (RD + 1)] = vfrag(tV, i + RD);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[i >> 2] = TR::mfma(ring[i % (RD + 1)], pb[(i >> 1) & 1][i & 1], acc[i >> 2]);
+      valu(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const float mb = m_run * c2;
-    float rs = 0.f;
+  };
+  // Masks, needed only on a wave's last tile (the ragged end of the keys, or the tile that
+  // holds this wave's diagonal): masked scores become -inf, so exp2 (with c2 > 0) makes
+  // exact zeros.
+  auto mask = [&](int j, f32x16 (&s)[2]) {
+    const int kv0 = j * BC;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[kb][i], c2, -mb));
-        s[kb][i] = p;
-        rs += p;
+        const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+        if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
       }
-    l_run += rs;
-
-    // ---- P^T operands: slot j of (kb, t2) = P for key kv0 + kb*32 + t2*16 + g*8 + j
-    u32x4 pb[2][2];
+  };
+  // Online softmax in raw-score units (c2 = scale * log2(e) > 0), as units u of work (see
+  // sm_step).  The reference max moves only when the tile max exceeds it by more than
+  // 2^kRescaleLog2 in the exp2 domain (always on the first tile); otherwise probabilities up
+  // to 2^kRescaleLog2 accumulate against the stale reference, exact because O and l share
+  // it.  When it moves, O is scaled by alpha at the start of the next step, after the P V
+  // products issued in this step.
+  bool need = false;  // uniform: O must be scaled by alpha before the next P V
+  float alpha = 1.f;
+  float mx0 = 0.f, mx1 = 0.f, mb = 0.f;
+  auto softmax_unit = [&](f32x16 (&s)[2], int u) {
+    if (u < kSmMax) {  // two running maxima, one per 32-key block, three-way max each
+      const int kb = u >> 3, e = (u & 7) * 2;
+      float& m = kb ? mx1 : mx0;
+      if ((u & 7) == 0)
+        m = fmaxf(s[kb][0], s[kb][1]);
+      else
+        m = fmaxf(m, fmaxf(s[kb][e], s[kb][e + 1]));
+    } else if (u == kSmRed) {
+      const float mx = pair_max(fmaxf(mx0, mx1));
+      const float m_new = fmaxf(m_run, mx);  // finite: key 0 is visible to every row
+      need = __builtin_amdgcn_ballot_w64((m_new - m_run) * c2 > kRescaleLog2) != 0;
+      alpha = need ? fast_exp2((m_run - m_new) * c2) : 1.f;
+      m_run = need ? m_new : m_run;
+      l_run *= alpha;
+      mb = m_run * c2;
+    } else {
+      const int e = u - kSmExp0, kb = e >> 4, i = e & 15;
+      s[kb][i] = fast_exp2(fmaf(s[kb][i], c2, -mb));
+    }
+  };
+  auto softmax_all = [&](f32x16 (&s)[2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int i0 = t2 * 8;
-        pb[kb][t2] = u32x4{TR::pack(s[kb][i0 + 0], s[kb][i0 + 1]), TR::pack(s[kb][i0 + 2], s[kb][i0 + 3]),
-                           TR::pack(s[kb][i0 + 4], s[kb][i0 + 5]), TR::pack(s[kb][i0 + 6], s[kb][i0 + 7])};
-      }
-
-    // ---- O^T += V^T P^T  (A = V^T: rows d, k = keys, read transposed from the V tile)
-    pipelined<DB * 4, 2>(
-        [&](int i) {
-          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
-          return lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl);
-        },
-        [&](int i, const u32x4& a) {
-          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
-          acc[db] = TR::mfma(a, pb[kb][t2], acc[db]);
-        });
+    for (int u = 0; u < kSmUnits; ++u) softmax_unit(s, u);
+  };
+  // P^T operands (slot j of (kb, t2) = P for key kb*32 + t2*16 + g*8 + j) and the row sum,
+  // as 16 units: unit i packs pair i%4 of operand (i/8, (i/4)%2) and adds its two values.
+  float rs = 0.f;
+  auto pack_unit = [&](u32x4 (&pb)[2][2], int i) {
+    const int kb = i >> 3, t2 = (i >> 2) & 1, pr = i & 3, e = t2 * 8 + pr * 2;
+    pb[kb][t2][pr] = TR::pack(p[kb][e], p[kb][e + 1]);
+    rs += p[kb][e] + p[kb][e + 1];
   };
 
-  // Unrolled by two so that each half sees fixed buffers (even tiles in buffer 0).
-  for (int t = 0; t < kv_end; t += 2) {
-    wait_vmcnt<0>();  // this wave's share of tile t has landed
-    lds_barrier();    // ... and everyone's; everyone is also done with tile t-1
-    step(t, sK + TILE, sV + TILE, sK, sV);
-    if (t + 1 < kv_end) {
-      wait_vmcnt<0>();
-      lds_barrier();
-      step(t + 1, sK, sV, sK + TILE, sV + TILE);
+  // Pipeline step j (0 <= j <= T), one per K/V tile plus a drain: waits for K_j and V_{j-1},
+  // loads K_{j+1} and V_j, then (by the kind of step) computes S_j and its softmax and/or
+  // P_{j-1} V_{j-1}.  The LDS buffers are restrict-qualified parameters so that the compiler
+  // can tell these reads from the direct loads in flight and does not make them wait.
+  enum Kind { kFirst, kFirstMasked, kSteady, kSteadyMasked, kDrain, kIdle };
+  auto step = [&](auto kind_tag, const int j, char* __restrict__ nK, char* __restrict__ nV,
+                  const char* __restrict__ tK, const char* __restrict__ tV) {
+    constexpr Kind KIND = decltype(kind_tag)::value;
+    wait_vmcnt<0>();  // this wave's loads of K_j and V_{j-1} have landed
+    lds_barrier();    // ... and everyone's; everyone is also done with step j-1's buffers
+    if (need) {       // the max moved in the previous step: rescale O (rare)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      need = false;
     }
+    if (j + 1 < T) issue(rK, j + 1, nK);
+    if (j < T) issue(rV, j, nV);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KIND == kSteady || KIND == kSteadyMasked) {
+      // [S_j MFMAs | pack P_{j-1}]  [P_{j-1} V_{j-1} MFMAs | softmax of S_j]
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      u32x4 pb[2][2];
+      rs = 0.f;
+      scores(tK, s, [&](int i) {
+#pragma unroll
+        for (int u = i * 16 / (2 * KST); u < (i + 1) * 16 / (2 * KST); ++u) pack_unit(pb, u);
+      });
+      l_run += rs;
+      if constexpr (KIND == kSteadyMasked) mask(j, s);
+      pv(tV, pb, [&](int i) {
+#pragma unroll
+        for (int u = 0; u < kSmUnits; ++u)
+          if (sm_step(u, DB * 4) == i) softmax_unit(s, u);
+      });
+      p[0] = s[0];
+      p[1] = s[1];
+    } else if constexpr (KIND == kFirst || KIND == kFirstMasked) {
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      scores(tK, s, [](int) {});
+      if constexpr (KIND == kFirstMasked) mask(j, s);
+      softmax_all(s);
+      need = false;  // O is still zero
+      p[0] = s[0];
+      p[1] = s[1];
+    } else if constexpr (KIND == kDrain) {
+      u32x4 pb[2][2];
+      rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pack_unit(pb, i);
+      l_run += rs;
+      pv(tV, pb, [](int) {});
+    }
+  };
+
+  // Buffers: step j reads K_j from kc and V_{j-1} from vp, and fills kn with K_{j+1} and vc
+  // with V_j; then the roles swap.
+  char* kc = sK;
+  char* kn = sK + TILE;
+  char* vc = sV;
+  char* vp = sV + TILE;
+  auto run = [&](auto kind_tag, int j) {
+    step(kind_tag, j, kn, vc, kc, vp);
+    char* t;
+    t = kc, kc = kn, kn = t;
+    t = vc, vc = vp, vp = t;
+  };
+  using KFirst = std::integral_constant<Kind, kFirst>;
+  using KFirstMasked = std::integral_constant<Kind, kFirstMasked>;
+  using KSteady = std::integral_constant<Kind, kSteady>;
+  using KSteadyMasked = std::integral_constant<Kind, kSteadyMasked>;
+  using KDrain = std::integral_constant<Kind, kDrain>;
+  using KIdle = std::integral_constant<Kind, kIdle>;
+  // Every wave takes exactly T + 1 steps (one barrier each); a wave's last computed tile
+  // Tw - 1 is the only one that can need masks.
+  if (Tw == 0) {
+    for (int j = 0; j <= T; ++j) run(KIdle{}, j);
+  } else {
+    if (Tw == 1)
+      run(KFirstMasked{}, 0);
+    else
+      run(KFirst{}, 0);
+    for (int j = 1; j < Tw - 1; ++j) run(KSteady{}, j);
+    if (Tw >= 2) run(KSteadyMasked{}, Tw - 1);
+    run(KDrain{}, Tw);
+    for (int j = Tw + 1; j <= T; ++j) run(KIdle{}, j);
+  }
+  if (need) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
   }
 
   // ---- epilogue: normalise, write O (input dtype, RNE) and LSE (natural log, fp32)
