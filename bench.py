@@ -2,22 +2,28 @@
 """Benchmark of the fused exact-attention hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input: the forward
-(fa_fwd) and the backward (preprocess, main, postprocess) on the same stream.  Inputs,
-outputs and workspace are allocated and resident in HBM before timing starts.
+(fa_fwd) and the backward (preprocess, dK/dV pass, dQ pass, postprocess) on the same stream.
+Inputs, outputs and workspace are allocated and resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout:
   value           whole-step attention TFLOP/s (fwd+bwd algorithmic FLOPs / step time)
   fwd_tflops ...  the forward and backward alone, and both as % of the bf16 dense MFMA peak
   roofline        the dominant kernel (largest share of step time), timed with HIP events
-                  on its own stream, against the MFMA peak
+                  on the stream it is launched on, against the MFMA peak; `traffic` is its HBM
+                  bytes per launch from the committed hardware-counter summary under profiles/,
+                  or null when the kernel source has changed since the counters were taken
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
 
 FLOP convention: forward 4*B*H*N^2*D, backward 10*B*H*N^2*D (five N x N x D products,
 including the recompute of S), halved when causal.
+
+`--copy-calibration BYTES` instead runs a plain device-to-device copy of BYTES bytes five
+times (the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -40,6 +46,56 @@ WORKLOAD_KEYS = {
 }
 for _i, (_n, _d) in enumerate([(2048, 64), (2048, 128), (4096, 64), (4096, 128), (4000, 64), (4000, 128)]):
     WORKLOAD_KEYS[f"gqa_causal_fp16_n{_n}_d{_d}"] = ("gqa_causal_fp16", _i)
+
+
+# Which sources each timed kernel is built from (for matching a counter summary to the code).
+KERNEL_SOURCES = {
+    "fwd": ["exact_attention_fa_amd/csrc/fa_fwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
+    "bwd_preprocess": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
+    "bwd_dkdv": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
+    "bwd_dq": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
+    "bwd_postprocess": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
+}
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt (key = value lines),
+    if that summary was taken on the current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256_16") != source_hash(kernel) or "hbm_bytes_per_launch" not in kv:
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def copy_calibration(nbytes):
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"copy_bytes": n * 4, "launches": 5, "ms_per_copy": round(dt * 1e3, 4),
+                      "read_plus_write_GBs": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
 
 
 def flops(shape, fwd=True, bwd=True):
@@ -94,12 +150,17 @@ def main():
     ap.add_argument("--workload", default="fwd_bf16_n4096", choices=sorted(WORKLOAD_KEYS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (attention heads and "
-              "batches shard with no communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "batches shard with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     import exact_attention_fa_amd as fa
@@ -169,14 +230,15 @@ def main():
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     dominant = max(kernels, key=lambda kname: avg[kname])
     # Algorithmic FLOPs per launch: the dK/dV pass does four of the backward's five N x N x D
-    # products (S, dP, dV, dK); the dQ pass recomputes S and dP and does dQ (three).
-    kflops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.6 * f_bwd,
+    # products (S, dP, dV, dK); the dQ pass adds the fifth (dQ).  Its recompute of S and dP
+    # (another 0.4 of the backward's FLOPs) is work this design adds, so it is not credited.
+    kflops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.2 * f_bwd,
               "bwd_preprocess": 0.0, "bwd_postprocess": 0.0}
     if kflops[dominant] > 0:
         achieved = kflops[dominant] / (avg[dominant] * 1e-3) / 1e12
         roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                    "traffic": None, "avg_ms": round(avg[dominant], 4)}
+                    "traffic": measured_traffic(dominant, args.workload), "avg_ms": round(avg[dominant], 4)}
     else:  # pragma: no cover - the contractions dominate every listed workload
         roofline = None
 

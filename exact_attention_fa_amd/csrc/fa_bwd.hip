@@ -35,7 +35,7 @@ constexpr int kThreads = 256;
 constexpr int kBwdBKV = 128;  // keys per workgroup (32 per wave)
 constexpr int kBwdBQ = 64;    // query rows per streamed tile
 constexpr int kDqBR = 128;    // dQ kernel: query rows per workgroup (32 per wave)
-constexpr int kDqBC = 64;     // dQ kernel: keys per K/V tile
+constexpr int kDqBC = 32;     // dQ kernel: keys per K/V tile
 
 // ---------------------------------------------------------------- preprocess
 // D[row] = sum_d dO[row][d] * O[row][d] (fp32) and L2[row] = LSE[row] * log2(e) (the
@@ -67,6 +67,15 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Key-stationary: a workgroup (4 waves) owns 128 keys of one query head, a wave owns 32.  The
+// wave's K and V rows are loaded once into registers (the B operands of S = Q K^T and
+// dP = dO V^T).  64-query tiles of Q and dO with their LSE*log2(e) and D stream through a
+// triple-buffered LDS by direct loads issued two tiles ahead, one barrier per tile.  Work is
+// done in units of 32 queries, software-pipelined inside the wave: while the MFMAs of S and
+// dP of unit u+1 run, the VALU forms P and dS of unit u; then the MFMAs of dV += P^T dO and
+// dK += dS^T Q of unit u run with dO and Q read transposed from LDS.  Query rows past the
+// end read as zero (Q = dO = 0 and LSE = D = 0), which makes their dS and dO rows zero: they
+// add nothing, so only the causal diagonal needs masks.
 template <typename TR, int HD, bool CAUSAL, bool PARTIAL>
 __global__ void __launch_bounds__(kThreads, 1)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -76,19 +85,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 int N, int n_kt, float c2, float scale) {
   constexpr int BKV = kBwdBKV, BQ = kBwdBQ;
   constexpr int KST = HD / 16, DB = HD / 32;
-  constexpr int KT_BYTES = BKV * HD * 2;
   constexpr int QT_BYTES = BQ * HD * 2;
-  constexpr int KI = KT_BYTES / 1024 / 4;   // 1 KB direct loads per wave for the K tile
-  constexpr int QI = QT_BYTES / 1024 / 4;   // ... for one Q (or dO) tile
-  static_assert(KI * 4096 == KT_BYTES && QI * 4096 == QT_BYTES, "tiles must split into 1 KB loads");
+  constexpr int QI = QT_BYTES / 1024 / 4;   // 1 KB direct loads per wave for one Q (or dO) tile
+  static_assert(QI * 4096 == QT_BYTES, "tiles must split into 1 KB loads");
+  constexpr int NBUF = 3;
+  constexpr int RD = 4;                     // LDS operand reads issued this many MFMAs ahead
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KT_BYTES + 4 * QT_BYTES + 4 * BQ * 4];
-  char* const sK = smem;
-  char* const sV = sK + KT_BYTES;
-  char* const sQ = sV + KT_BYTES;          // two buffers
-  char* const sdO = sQ + 2 * QT_BYTES;     // two buffers
-  char* const sL = sdO + 2 * QT_BYTES;     // two buffers of BQ floats: LSE * log2(e)
-  char* const sD = sL + 2 * BQ * 4;        // two buffers of BQ floats: D
+  // NBUF slots, each [Q tile | dO tile | BQ floats LSE*log2(e) | BQ floats D].
+  constexpr int SLOT = 2 * QT_BYTES + 2 * BQ * 4;
+  constexpr int OFF_DO = QT_BYTES, OFF_L = 2 * QT_BYTES, OFF_D = 2 * QT_BYTES + BQ * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,8 +107,6 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int hq = bh % Hq, b = bh / Hq;
   const int hkv = hq / (Hq / Hkv);
   const size_t kvoff = ((size_t)b * Hkv + hkv) * N * HD;
-  const uint16_t* const Kh = K + kvoff;
-  const uint16_t* const Vh = V + kvoff;
   const uint16_t* const Qh = Q + (size_t)bh * N * HD;
   const uint16_t* const dOh = dO + (size_t)bh * N * HD;
   const float* const L2h = L2 + (size_t)bh * N;
@@ -114,8 +118,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int n_qt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kv0 / BQ : 0;  // earlier query tiles see none of these keys
 
-  // Direct loads of one 64-query tile of Q, dO, L2 and D into buffer `buf`.  Rows past the
-  // end read as zero (their scores are masked).
+  // Direct loads of one 64-query tile of Q, dO, L2 and D into buffer slot `sl`.
   const uint32_t rowb = (uint32_t)N * HD * 2u;
   const BufRes rQ = make_bufres(Qh, rowb), rdO = make_bufres(dOh, rowb);
   const BufRes rL = make_bufres(L2h, (uint32_t)N * 4u), rD = make_bufres(Dh, (uint32_t)N * 4u);
@@ -126,42 +129,33 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     sl_pos_to_rc<BQ>((uint32_t)((wave * QI + r) * 64 + lane), row, col);
     qvo[r] = (uint32_t)(row * HD + col) * 2u;
   }
-  auto issue = [&](int qt, char* dQt, char* ddO, char* dL, char* dD) {
+  auto issue = [&](int qt, char* dst) FA_INL {
     const uint32_t q0 = (uint32_t)qt * BQ;
 #pragma unroll
     for (int r = 0; r < QI; ++r) {
       const int blk = wave * QI + r;
-      dma_to_lds<16>(rQ, qvo[r], q0 * (HD * 2), dQt + blk * 1024);
-      dma_to_lds<16>(rdO, qvo[r], q0 * (HD * 2), ddO + blk * 1024);
+      dma_to_lds<16>(rQ, qvo[r], q0 * (HD * 2), dst + blk * 1024);
+      dma_to_lds<16>(rdO, qvo[r], q0 * (HD * 2), dst + OFF_DO + blk * 1024);
     }
-    if (wave == 0) dma_to_lds<4>(rL, (uint32_t)lane * 4u, q0 * 4u, dL);
-    if (wave == 1) dma_to_lds<4>(rD, (uint32_t)lane * 4u, q0 * 4u, dD);
+    if (wave == 0) dma_to_lds<4>(rL, (uint32_t)lane * 4u, q0 * 4u, dst + OFF_L);
+    if (wave == 1) dma_to_lds<4>(rD, (uint32_t)lane * 4u, q0 * 4u, dst + OFF_D);
   };
+  if (qt0 < n_qt) issue(qt0, smem);
+  if (qt0 + 1 < n_qt) issue(qt0 + 1, smem + SLOT);
 
-  // K and V tiles -> LDS for the whole kernel (keys past the end read as zero; their scores
-  // are masked), then the first query tile.
-  {
-    const BufRes rK = make_bufres(Kh, rowb), rV = make_bufres(Vh, rowb);
+  // K and V rows of this lane's key as B operands: slot j of k-step kk = K[key][kk*16 + g*8 + j]
+  // (zero past the end: those keys' dK/dV are never stored).
+  u32x4 kf[KST], vf[KST];
 #pragma unroll
-    for (int r = 0; r < KI; ++r) {
-      const int blk = wave * KI + r;
-      int row, col;
-      sl_pos_to_rc<BKV>((uint32_t)(blk * 64 + lane), row, col);
-      const uint32_t vo = (uint32_t)(row * HD + col) * 2u;
-      dma_to_lds<16>(rK, vo, (uint32_t)kv0 * (HD * 2), sK + blk * 1024);
-      dma_to_lds<16>(rV, vo, (uint32_t)kv0 * (HD * 2), sV + blk * 1024);
-    }
+  for (int kk = 0; kk < KST; ++kk) {
+    kf[kk] = ld16_if(K + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
+    vf[kk] = ld16_if(V + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
   }
-  if (qt0 < n_qt) issue(qt0, sQ, sdO, sL, sD);
 
-  // Per-lane LDS offsets (all reads below add compile-time tile offsets to these).
-  const uint32_t poff[2] = {sl_off<64>(c, g * 8), sl_off<64>(c, 16 + g * 8)};                   // row c
-  const uint32_t qoff[2] = {sl_off<64>(perm_rows(c), g * 8), sl_off<64>(perm_rows(c), 16 + g * 8)};  // permuted
+  // Per-lane LDS offsets: Q/dO rows in the permuted order, so register i of a unit's S/dP
+  // block is query (i/8)*16 + g*8 + i%8; one offset per k-step parity.
+  const uint32_t qoff[2] = {sl_off<BQ>(perm_rows(c), g * 8), sl_off<BQ>(perm_rows(c), 16 + g * 8)};
   const TrLane trl = tr_lane(lane);
-
-  wait_vmcnt<0>();
-  lds_barrier();
-  // B operands of S = Q K^T and dP = dO V^T for k-step kk: slot j = K/V[key][kk*16 + g*8 + j]
 
   f32x16 dKa[DB], dVa[DB];
 #pragma unroll
@@ -170,138 +164,174 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     dVa[db] = f32x16{};
   }
 
-  // One 64-query tile: recompute S and P, form dP and dS, accumulate dV and dK.  Register i of the accumulators of query block qb is
-  // query q0 + qb*32 + (i/8)*16 + g*8 + i%8 (permuted Q/dO rows), key `key`; that order is
-  // the k-slot order of the A operands of dV = P^T dO and dK = dS^T Q.  The MASKED body
-  // handles the causal diagonal and ragged edges; the other one is straight-line code so the
-  // two query blocks' MFMAs and softmax work can be interleaved by the scheduler.
-  auto tile = [&](auto masked_tag, const int q0, const char* tQ, const char* tdO, const float* tL,
-                  const float* tD, const char* tK, const char* tV) {
+  // ---- pipeline pieces.  A unit is (query tile qt, block qb): queries qt*BQ + qb*32 + 0..31,
+  //      held in the LDS slot `sl` of its tile.
+  // S = Q K^T and dP = dO V^T of a unit (16 MFMAs), with valu(i) under MFMA i.
+  auto sdp = [&](const char* sl, int qb, f32x16& s, f32x16& dp, auto&& valu) FA_INL {
+    const char* tQ = sl;
+    const char* tdO = sl + OFF_DO;
+    auto frag = [&](int i) FA_INL {  // i = kk*2 + (0: Q, 1: dO)
+      const int kk = i >> 1;
+      const uint32_t o = sl_off<BQ>(qb * 32, (kk >> 1) * 32) + qoff[kk & 1];
+      return lds_ld128(((i & 1) ? tdO : tQ) + o);
+    };
+    u32x4 ring[RD + 1];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < 2 * KST; ++i) {
+      if (i + RD < 2 * KST) ring[(i + RD) % (RD + 1)] = frag(i + RD);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i & 1)
+        dp = TR::mfma(ring[i % (RD + 1)], vf[i >> 1], dp);
+      else
+        s = TR::mfma(ring[i % (RD + 1)], kf[i >> 1], s);
+      valu(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // LSE*log2(e) and D of the unit's queries as this lane's registers see them:
+  // l[t2*2 + h][e] is query qb*32 + t2*16 + g*8 + h*4 + e.
+  struct RowVals {
+    f32x4 l[4], d[4];
+  };
+  auto rowvals = [&](const char* sl, int qb) FA_INL {
+    RowVals r;
+    const float* tL = reinterpret_cast<const float*>(sl + OFF_L);
+    const float* tD = reinterpret_cast<const float*>(sl + OFF_D);
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = qb * 32 + t2 * 16 + g * 8 + h * 4;
+        r.l[t2 * 2 + h] = *reinterpret_cast<const f32x4*>(tL + q);
+        r.d[t2 * 2 + h] = *reinterpret_cast<const f32x4*>(tD + q);
+      }
+    return r;
+  };
+  // P = exp2(S c2 - LSE log2 e) and dS = P (dP - D) of one unit as 16 work units (one query
+  // register each), packed into the A operands of dV += P^T dO and dK += dS^T Q.
+  auto pds_unit = [&](f32x16& s, const f32x16& dp, const RowVals& rv, u32x4 (&pa)[2], u32x4 (&dsa)[2],
+                      float (&pt)[2], float (&dt)[2], int i) FA_INL {
+    const int t2 = i >> 3, j = i & 7;
+    const float lse2 = rv.l[t2 * 2 + (j >> 2)][j & 3];
+    const float dd = rv.d[t2 * 2 + (j >> 2)][j & 3];
+    const float p = fast_exp2(fmaf(s[i], c2, -lse2));
+    const float ds = p * (dp[i] - dd);
+    if (j & 1) {
+      pa[t2][j >> 1] = TR::pack(pt[0], p);
+      dsa[t2][j >> 1] = TR::pack(dt[0], ds);
+    } else {
+      pt[0] = p;
+      dt[0] = ds;
+    }
+  };
+  // Causal mask of a unit whose queries start at q0: keys after the query get -inf.
+  auto mask = [&](f32x16& s, int q0) FA_INL {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = q0 + (i >> 3) * 16 + g * 8 + (i & 7);
+      if (key > q) s[i] = -INFINITY;
+    }
+  };
+  // dV += P^T dO and dK += dS^T Q of a unit (16 MFMAs); B operands read transposed.
+  auto dvdk = [&](const char* sl, int qb, const u32x4 (&pa)[2], const u32x4 (&dsa)[2]) FA_INL {
+    const char* tQ = sl;
+    const char* tdO = sl + OFF_DO;
+    auto frag = [&](int i) FA_INL {  // i = (db*2 + t2)*2 + (0: dO, 1: Q)
+      const int db = i >> 2, t2 = (i >> 1) & 1;
+      const uint32_t o = sl_off<BQ>(qb * 32 + t2 * 16, db * 32);
+      return lds_tr8(((i & 1) ? tQ : tdO) + o, trl);
+    };
+    u32x4 ring[RD + 1];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      if (i + RD < 4 * DB) ring[(i + RD) % (RD + 1)] = frag(i + RD);
+      __builtin_amdgcn_sched_barrier(0);
+      const int db = i >> 2, t2 = (i >> 1) & 1;
+      if (i & 1)
+        dKa[db] = TR::mfma(dsa[t2], ring[i % (RD + 1)], dKa[db]);
+      else
+        dVa[db] = TR::mfma(pa[t2], ring[i % (RD + 1)], dVa[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // One pipeline iteration for unit (qt, qb) held in slot `sl`: [S/dP of the next unit, held
+  // in `nsl` | P, dS of this unit] then [dV, dK of this unit].  (cs, cdp) hold this unit's
+  // S/dP, (ns, ndp) receive the next one's.
+  auto unit = [&](auto masked_tag, auto has_next_tag, int qt, int qb, const char* sl, const char* nsl,
+                  f32x16& cs, f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    // ---- S = Q K^T and dP = dO V^T for both query blocks, k-step by k-step
-    struct Ops1 {
-      u32x4 kf, vf, q[2], o[2];
-    };
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    pipelined<KST, 2>(
-        [&](int kk) {
-          Ops1 f;
-          const uint32_t ko = sl_off<BKV>(wave * 32, (kk >> 1) * 32) + poff[kk & 1];
-          f.kf = lds_ld128(tK + ko);
-          f.vf = lds_ld128(tV + ko);
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    const RowVals rv = rowvals(sl, qb);
+    if constexpr (MASKED) mask(cs, qt * BQ + qb * 32);
+    u32x4 pa[2], dsa[2];
+    float pt[2], dt[2];
+    if constexpr (HAS_NEXT) {
+      ns = f32x16{};
+      ndp = f32x16{};
+      sdp(nsl, qb ^ 1, ns, ndp, [&](int i) FA_INL {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const uint32_t o = sl_off<BQ>(qb * 32, (kk >> 1) * 32) + qoff[kk & 1];
-            f.q[qb] = lds_ld128(tQ + o);
-            f.o[qb] = lds_ld128(tdO + o);
-          }
-          return f;
-        },
-        [&](int, const Ops1& f) {
+        for (int w = 0; w < 16; ++w)
+          if (w * 2 * KST / 16 == i) pds_unit(cs, cdp, rv, pa, dsa, pt, dt, w);
+      });
+    } else {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = TR::mfma(f.q[qb], f.kf, s[qb]);
-            dp[qb] = TR::mfma(f.o[qb], f.vf, dp[qb]);
-          }
-        });
-
-    // ---- P = exp2(S c2 - LSE log2 e), dS = P (dP - D); rounded copies are the A operands of
-    //      dV += P^T dO and dK += dS^T Q.
-    u32x4 pa[2][2], dsa[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qb0 = q0 + qb * 32;
-      if (MASKED) {
-        // masked scores become -inf, so exp2 (with c2 > 0) makes them exact zeros
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = qb0 + (i >> 3) * 16 + g * 8 + (i & 7);
-          if (key >= N || q >= N || (CAUSAL && key > q)) s[qb][i] = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int r0 = qb * 32 + t2 * 16 + g * 8;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(tL + r0);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(tL + r0 + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(tD + r0);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(tD + r0 + 4);
-        float p[8], ds[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = t2 * 8 + j;
-          const float lse2 = j < 4 ? l0[j] : l1[j - 4];
-          const float dd = j < 4 ? d0[j] : d1[j - 4];
-          p[j] = fast_exp2(fmaf(s[qb][i], c2, -lse2));
-          ds[j] = p[j] * (dp[qb][i] - dd);
-        }
-        pa[qb][t2] = u32x4{TR::pack(p[0], p[1]), TR::pack(p[2], p[3]), TR::pack(p[4], p[5]), TR::pack(p[6], p[7])};
-        dsa[qb][t2] = u32x4{TR::pack(ds[0], ds[1]), TR::pack(ds[2], ds[3]), TR::pack(ds[4], ds[5]),
-                            TR::pack(ds[6], ds[7])};
-      }
+      for (int w = 0; w < 16; ++w) pds_unit(cs, cdp, rv, pa, dsa, pt, dt, w);
     }
-
-    // ---- dV += P^T dO, dK += dS^T Q; B operands read transposed from the dO / Q tiles
-    struct Ops2 {
-      u32x4 o, q;
-    };
-    pipelined<2 * DB * 2, 2>(
-        [&](int i) {
-          const int qb = i / (2 * DB), db = (i / 2) % DB, t2 = i % 2;
-          const uint32_t o = sl_off<BQ>(qb * 32 + t2 * 16, db * 32);
-          return Ops2{lds_tr8(tdO + o, trl), lds_tr8(tQ + o, trl)};
-        },
-        [&](int i, const Ops2& f) {
-          const int qb = i / (2 * DB), db = (i / 2) % DB, t2 = i % 2;
-          dVa[db] = TR::mfma(pa[qb][t2], f.o, dVa[db]);
-          dKa[db] = TR::mfma(dsa[qb][t2], f.q, dKa[db]);
-        });
+    dvdk(sl, qb, pa, dsa);
   };
 
-  // One query tile: wait for its loads, prefetch the next, compute.  The LDS buffers are
-  // restrict-qualified parameters so that the compiler can tell this tile's reads from the
-  // direct loads filling the next tile and does not make them wait.
-  auto step = [&](auto masked_tag, const int qt, char* __restrict__ nQ, char* __restrict__ ndO,
-                  char* __restrict__ nL, char* __restrict__ nD, const char* __restrict__ tQ,
-                  const char* __restrict__ tdO, const char* __restrict__ tL, const char* __restrict__ tD,
-                  const char* __restrict__ tK, const char* __restrict__ tV) {
-    const int q0 = qt * BQ;
-    if (qt > qt0) {
-      wait_vmcnt<0>();  // this tile's direct loads (issued one tile ago) have landed
-      lds_barrier();    // ... for every wave; every wave is also done with the previous tile
-    }
-    if (qt + 1 < n_qt) issue(qt + 1, nQ, ndO, nL, nD);
+  // Per query tile: wait for its successor's loads and let every wave see them (everyone is
+  // then also done with the tile two back, whose slot the next loads refill), then two units.
+  // The slots are restrict-qualified parameters so that the compiler can tell these reads
+  // from the direct loads in flight and does not make them wait.
+  f32x16 s0, dp0, s1, dp1;
+  auto tile = [&](auto masked_tag, auto last_tag, int qt, char* __restrict__ cur, char* __restrict__ nxt,
+                  char* __restrict__ dst) FA_INL {
+    constexpr bool LAST = decltype(last_tag)::value;
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (qt + 2 < n_qt) issue(qt + 2, dst);
     __builtin_amdgcn_sched_barrier(0);
-    tile(masked_tag, q0, tQ, tdO, reinterpret_cast<const float*>(tL), reinterpret_cast<const float*>(tD), tK, tV);
+    unit(masked_tag, std::true_type{}, qt, 0, cur, cur, s0, dp0, s1, dp1);
+    if constexpr (LAST)
+      unit(masked_tag, std::false_type{}, qt, 1, cur, nxt, s1, dp1, s0, dp0);
+    else
+      unit(masked_tag, std::true_type{}, qt, 1, cur, nxt, s1, dp1, s0, dp0);
   };
 
-  // Query tiles [qt_a, qt_b) need no mask for any wave of the workgroup (the key tile is
-  // whole, the query tile is whole and lies entirely below the diagonal); the others take
-  // the masked body.  Three single-body loops keep the accumulators in fixed registers.
-  int qt_a = qt0, qt_b = qt0;
-  if (kv0 + BKV <= N) {
-    qt_a = CAUSAL ? min(n_qt, (kv0 + BKV - 1) / BQ + 1) : qt0;  // first tile with q0 >= kv0 + BKV - 1
-    qt_b = max(qt_a, N / BQ);                                   // tiles before the ragged tail
+  if (qt0 < n_qt) {
+    // prologue: S/dP of the first unit
+    wait_vmcnt<0>();
+    lds_barrier();
+    s0 = f32x16{};
+    dp0 = f32x16{};
+    sdp(smem, 0, s0, dp0, [](int) FA_INL {});
+    char* c0 = smem;
+    char* c1 = smem + SLOT;
+    char* c2 = smem + 2 * SLOT;
+    auto run = [&](auto masked_tag, auto last_tag, int qt) FA_INL {
+      tile(masked_tag, last_tag, qt, c0, c1, c2);
+      char* t = c0;
+      c0 = c1;
+      c1 = c2;
+      c2 = t;
+    };
+    // causal: the first two tiles hold this workgroup's diagonal; every later tile is
+    // entirely below it
+    const int qt_m = CAUSAL ? min(n_qt, qt0 + 2) : qt0;
+    int qt = qt0;
+    for (; qt < qt_m && qt < n_qt - 1; ++qt) run(std::true_type{}, std::false_type{}, qt);
+    for (; qt < n_qt - 1; ++qt) run(std::false_type{}, std::false_type{}, qt);
+    if (qt < qt_m)
+      run(std::true_type{}, std::true_type{}, qt);
+    else
+      run(std::false_type{}, std::true_type{}, qt);
   }
-  char* cQ = sQ;
-  char* cdO = sdO;
-  char* cL = sL;
-  char* cD = sD;
-  char* nQ = sQ + QT_BYTES;
-  char* ndO = sdO + QT_BYTES;
-  char* nL = sL + BQ * 4;
-  char* nD = sD + BQ * 4;
-  auto run = [&](auto masked_tag, int qt) {
-    step(masked_tag, qt, nQ, ndO, nL, nD, cQ, cdO, cL, cD, sK, sV);
-    char* t;
-    t = cQ, cQ = nQ, nQ = t;
-    t = cdO, cdO = ndO, ndO = t;
-    t = cL, cL = nL, nL = t;
-    t = cD, cD = nD, nD = t;
-  };
-  for (int qt = qt0; qt < qt_a; ++qt) run(std::true_type{}, qt);
-  for (int qt = qt_a; qt < qt_b; ++qt) run(std::false_type{}, qt);
-  for (int qt = max(qt_a, qt_b); qt < n_qt; ++qt) run(std::true_type{}, qt);
 
   // ---- epilogue: register i of dKa/dVa[db] <-> key kw0 + (i/4)*8 + g*4 + i%4, column db*32 + c
 #pragma unroll
@@ -325,13 +355,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
 // ---------------------------------------------------------------- dQ
 // Query-stationary: a workgroup owns 128 query rows (32 per wave) of one head and streams
-// the K/V tiles of its KV head through a double-buffered LDS, exactly like the forward.  Per
-// 64-key tile, per wave:
+// 32-key tiles of K and V of its KV head through LDS (direct loads issued three tiles ahead;
+// four K buffers, three V buffers; one barrier per tile).  Per tile j, per wave:
 //   S^T = K Q^T and dP^T = V dO^T  (K, V rows from LDS; Q and dO fragments in registers)
-//   P^T = exp2(S^T c2 - LSE log2 e),  dS^T = P^T * (dP^T - D)      (fp32, one query per lane)
+//   dS^T = exp2(S^T c2 - LSE log2 e) * (dP^T - D)        (fp32, one query per lane)
 //   dQ^T += K^T dS^T  (K^T read transposed from the K tile; the rounded dS^T registers are
 //                      the B operand thanks to the permuted K rows)
-// Every dQ element is produced by exactly one lane: no atomics, bitwise deterministic.
+// software-pipelined inside the wave: the VALU work of tile j runs under the MFMAs of S^T and
+// dP^T of tile j+1, then the dQ MFMAs of tile j follow.  Keys past the end read as zero rows
+// of K and V, so their dS^T K terms vanish; only the causal diagonal needs masks.  Every dQ
+// element is produced by exactly one lane: no atomics, bitwise deterministic.
 template <typename TR, int HD, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -344,10 +377,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
   constexpr int TI = TILE / 1024 / 4;       // 1 KB direct loads per wave per tile
   static_assert(TI * 4096 == TILE, "tile must split into 1 KB loads over 4 waves");
+  constexpr int NK = 4, NV = 3;             // K tiles j..j+3, V tiles j+1..j+3
+  constexpr int RD = 4;                     // LDS operand reads issued this many MFMAs ahead
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2], V[2]
-  char* const sK = smem;
-  char* const sV = smem + 2 * TILE;
+  __shared__ __attribute__((aligned(1024))) char smem[(NK + NV) * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -366,10 +399,15 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int qw0 = qt * BR + wave * 32;  // first query row of this wave
   const int qi = qw0 + c;               // the query of this lane's accumulator column
 
-  int kv_end = (N + BC - 1) / BC;
-  if (CAUSAL) kv_end = (min(N, (qt + 1) * BR) - 1) / BC + 1;
+  // Key tiles the workgroup streams, and the prefix this wave computes on (causal waves stop
+  // at the tile holding their diagonal; waves wholly past the last row compute nothing).
+  int T = (N + BC - 1) / BC;
+  if (CAUSAL) T = (min(N, (qt + 1) * BR) - 1) / BC + 1;
+  int Tw = T;
+  if (CAUSAL) Tw = (min(N, qw0 + 32) - 1) / BC + 1;
+  if (qw0 >= N) Tw = 0;
 
-  // Direct loads of K/V tile t (keys past the end read as zero; their scores are masked).
+  // Direct loads of K/V tile t (keys past the end read as zero).
   const BufRes rK = make_bufres(Kh, (uint32_t)N * HD * 2u), rV = make_bufres(Vh, (uint32_t)N * HD * 2u);
   uint32_t kvo[TI];
 #pragma unroll
@@ -378,7 +416,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     sl_pos_to_rc<BC>((uint32_t)((wave * TI + r) * 64 + lane), row, col);
     kvo[r] = (uint32_t)(row * HD + col) * 2u;
   }
-  auto issue = [&](int t, char* dK_, char* dV_) {
+  auto issue = [&](int t, char* dK_, char* dV_) FA_INL {
 #pragma unroll
     for (int r = 0; r < TI; ++r) {
       const int blk = wave * TI + r;
@@ -386,7 +424,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       dma_to_lds<16>(rV, kvo[r], (uint32_t)t * (BC * HD * 2), dV_ + blk * 1024);
     }
   };
-  issue(0, sK, sV);
+  char* const kb0 = smem;                // K buffers kb0 + i*TILE, i < NK
+  char* const vb0 = smem + NK * TILE;    // V buffers vb0 + i*TILE, i < NV
+  // tiles 0, 1, 2 go to K buffers 0, 1, 2 and V buffers 0, 1, 2
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (t < T) issue(t, kb0 + t * TILE, vb0 + t * TILE);
 
   // B operands: slot j of k-step kk = Q[qi][kk*16 + g*8 + j] and dO[qi][...]
   const size_t rowoff = (size_t)bh * N * HD + (size_t)qi * HD;
@@ -406,90 +449,158 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  auto step = [&](const int t, char* __restrict__ nK, char* __restrict__ nV, const char* __restrict__ tK,
-                  const char* __restrict__ tV) {
-    if (t + 1 < kv_end) issue(t + 1, nK, nV);
-    const int kv0 = t * BC;
-    if (CAUSAL && kv0 > qw0 + 31) return;  // tile lies above the diagonal for this wave
-
-    // ---- S^T = K Q^T, dP^T = V dO^T: register i of block kb is key kv0 + kb*32 + (i/8)*16 + g*8 + i%8
-    struct Ops {
-      u32x4 k[2], v[2];
+  // ---- pipeline pieces
+  // S^T and dP^T of one tile (register i <-> key (i/8)*16 + g*8 + i%8), with valu(i) run
+  // under MFMA i.
+  auto sdp = [&](const char* tK, const char* tV, f32x16& s, f32x16& dp, auto&& valu) FA_INL {
+    auto frag = [&](int i) FA_INL {  // i = kk*2 + (0: K, 1: V)
+      const int kk = i >> 1;
+      return lds_ld128(((i & 1) ? tV : tK) + sl_off<BC>(0, (kk >> 1) * 32) + koff[kk & 1]);
     };
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    pipelined<KST, 1>(
-        [&](int kk) {
-          Ops f;
+    u32x4 ring[RD + 1];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const uint32_t o = sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1];
-            f.k[kb] = lds_ld128(tK + o);
-            f.v[kb] = lds_ld128(tV + o);
-          }
-          return f;
-        },
-        [&](int kk, const Ops& f) {
+    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = TR::mfma(f.k[kb], qf[kk], s[kb]);
-            dp[kb] = TR::mfma(f.v[kb], of[kk], dp[kb]);
-          }
-        });
-
-    if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0)) {
-      // masked scores become -inf, so exp2 (with c2 > 0) makes them exact zeros
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-          if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
-        }
+    for (int i = 0; i < 2 * KST; ++i) {
+      if (i + RD < 2 * KST) ring[(i + RD) % (RD + 1)] = frag(i + RD);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i & 1)
+        dp = TR::mfma(ring[i % (RD + 1)], of[i >> 1], dp);
+      else
+        s = TR::mfma(ring[i % (RD + 1)], qf[i >> 1], s);
+      valu(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // ---- dS^T = P^T (dP^T - D), rounded to the B operand of dQ^T += K^T dS^T
-    u32x4 dsb[2][2];
+  };
+  // dS^T of tile j as 16 work units (one key register each), packed into the B operand of
+  // dQ^T += K^T dS^T.  Causal masks (keys after the query) on the wave's last tile only.
+  auto ds_unit = [&](auto masked_tag, int j, const f32x16& s, const f32x16& dp, u32x4 (&dsb)[2], float& dt,
+                     int i) FA_INL {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    float sv = s[i];
+    if constexpr (MASKED) {
+      const int key = j * BC + (i >> 3) * 16 + g * 8 + (i & 7);
+      if (key > qi) sv = -INFINITY;
+    }
+    const float ds = fast_exp2(fmaf(sv, c2, -l2)) * (dp[i] - dd);
+    if (i & 1)
+      dsb[i >> 3][(i & 7) >> 1] = TR::pack(dt, ds);
+    else
+      dt = ds;
+  };
+  // dQ^T += K^T dS^T of one tile (2*DB MFMAs), A operand read transposed from the K tile.
+  auto dqm = [&](const char* tK, const u32x4 (&dsb)[2]) FA_INL {
+    auto frag = [&](int i) FA_INL {  // i = db*2 + t2
+      return lds_tr8(tK + sl_off<BC>((i & 1) * 16, (i >> 1) * 32), trl);
+    };
+    constexpr int NS = 2 * DB;
+    u32x4 ring[RD + 1];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        float ds[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = t2 * 8 + j;
-          ds[j] = fast_exp2(fmaf(s[kb][i], c2, -l2)) * (dp[kb][i] - dd);
-        }
-        dsb[kb][t2] = u32x4{TR::pack(ds[0], ds[1]), TR::pack(ds[2], ds[3]), TR::pack(ds[4], ds[5]),
-                            TR::pack(ds[6], ds[7])};
-      }
-
-    // ---- dQ^T += K^T dS^T  (A = K^T: rows d, k = keys, read transposed from the K tile)
-    pipelined<DB * 4, 2>(
-        [&](int i) {
-          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
-          return lds_tr8(tK + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl);
-        },
-        [&](int i, const u32x4& a) {
-          const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
-          acc[db] = TR::mfma(a, dsb[kb][t2], acc[db]);
-        });
+    for (int i = 0; i < NS; ++i) {
+      if (i + RD < NS) ring[(i + RD) % (RD + 1)] = frag(i + RD);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[i >> 1] = TR::mfma(ring[i % (RD + 1)], dsb[i & 1], acc[i >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // Unrolled by two so that each half sees fixed buffers (even tiles in buffer 0).
-  for (int t = 0; t < kv_end; t += 2) {
-    wait_vmcnt<0>();
-    lds_barrier();
-    step(t, sK + TILE, sV + TILE, sK, sV);
-    if (t + 1 < kv_end) {
+  // Step j (0 <= j < T): wait for tile j+1 (tile j+2 may stay in flight), let every wave see
+  // it (everyone is then also done with step j-1, whose buffers the next loads refill), load
+  // tile j+3, then [S^T/dP^T of tile j+1 | dS^T of tile j] and dQ of tile j.  (cs, cdp) hold
+  // tile j's S^T/dP^T, (ns, ndp) receive tile j+1's.  The LDS buffers are restrict-qualified
+  // parameters so that the compiler can tell these reads from the loads in flight.
+  enum Kind { kSteady, kLast, kLastMasked, kIdle };
+  auto step = [&](auto kind_tag, const int j, const char* __restrict__ tK, const char* __restrict__ nK,
+                  const char* __restrict__ nV, char* __restrict__ dK_, char* __restrict__ dV_, f32x16& cs,
+                  f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
+    constexpr Kind KIND = decltype(kind_tag)::value;
+    if (j + 2 < T)
+      wait_vmcnt<2 * TI>();
+    else
       wait_vmcnt<0>();
-      lds_barrier();
-      step(t + 1, sK, sV, sK + TILE, sV + TILE);
+    lds_barrier();
+    if (j + 3 < T) issue(j + 3, dK_, dV_);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 dsb[2];
+    float dt;
+    if constexpr (KIND == kSteady) {
+      ns = f32x16{};
+      ndp = f32x16{};
+      sdp(nK, nV, ns, ndp, [&](int i) FA_INL {
+#pragma unroll
+        for (int w = 0; w < 16; ++w)
+          if (w * 2 * KST / 16 == i) ds_unit(std::false_type{}, j, cs, cdp, dsb, dt, w);
+      });
+      dqm(tK, dsb);
+    } else if constexpr (KIND == kLast || KIND == kLastMasked) {
+#pragma unroll
+      for (int w = 0; w < 16; ++w) ds_unit(std::bool_constant<KIND == kLastMasked>{}, j, cs, cdp, dsb, dt, w);
+      dqm(tK, dsb);
     }
-  }
+  };
 
-  // ---- epilogue: dQ = scale * acc; register i of acc[db] is column db*32 + (i/4)*8 + g*4 + i%4
+  // Buffer rings: K tiles j, j+1, j+2 and the slot for j+3; V tiles j+1, j+2 and the slot
+  // for j+3.
+  char* k0 = kb0;
+  char* k1 = kb0 + TILE;
+  char* k2 = kb0 + 2 * TILE;
+  char* k3 = kb0 + 3 * TILE;
+  char* v1 = vb0 + TILE;
+  char* v2 = vb0 + 2 * TILE;
+  char* v3 = vb0;
+  f32x16 sa, dpa, sb, dpb;
+  auto run = [&](auto kind_tag, int j, f32x16& cs, f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
+    step(kind_tag, j, k0, k1, v1, k3, v3, cs, cdp, ns, ndp);
+    char* t = k0;
+    k0 = k1;
+    k1 = k2;
+    k2 = k3;
+    k3 = t;
+    t = v1;
+    v1 = v2;
+    v2 = v3;
+    v3 = t;
+  };
+  using KSteady = std::integral_constant<Kind, kSteady>;
+  using KLast = std::integral_constant<Kind, CAUSAL ? kLastMasked : kLast>;
+  using KIdle = std::integral_constant<Kind, kIdle>;
+
+  // prologue: tile 0 resident (tiles 1 and 2 may stay in flight), S^T/dP^T of tile 0
+  if (T > 2)
+    wait_vmcnt<4 * TI>();
+  else if (T > 1)
+    wait_vmcnt<2 * TI>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+  if (Tw > 0) {
+    sa = f32x16{};
+    dpa = f32x16{};
+    sdp(kb0, vb0, sa, dpa, [](int) FA_INL {});
+  }
+  // Every wave takes exactly T steps (one barrier each); a wave's last computed tile Tw - 1
+  // is the only one that can need masks.
+  int j = 0;
+  for (; j + 2 <= Tw - 1; j += 2) {
+    run(KSteady{}, j, sa, dpa, sb, dpb);
+    run(KSteady{}, j + 1, sb, dpb, sa, dpa);
+  }
+  if (j < Tw - 1) {
+    run(KSteady{}, j, sa, dpa, sb, dpb);
+    ++j;
+    run(KLast{}, j, sb, dpb, sa, dpa);
+    ++j;
+  } else if (j == Tw - 1) {
+    run(KLast{}, j, sa, dpa, sb, dpb);
+    ++j;
+  }
+  for (; j < T; ++j) run(KIdle{}, j, sa, dpa, sb, dpb);
+
+  // ---- epilogue: register i of acc[db] <-> dQ[qi][db*32 + (i/4)*8 + g*4 + i%4]
   if (qi < N) {
-    uint16_t* const drow = dQ + rowoff;
+    uint16_t* const qrow = dQ + (size_t)bh * N * HD + (size_t)qi * HD;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -497,7 +608,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int d = db * 32 + i4 * 8 + g * 4;
         const u32x2 w = {TR::pack(acc[db][i4 * 4 + 0] * scale, acc[db][i4 * 4 + 1] * scale),
                          TR::pack(acc[db][i4 * 4 + 2] * scale, acc[db][i4 * 4 + 3] * scale)};
-        *reinterpret_cast<u32x2*>(drow + d) = w;
+        *reinterpret_cast<u32x2*>(qrow + d) = w;
       }
   }
 }

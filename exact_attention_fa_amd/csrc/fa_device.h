@@ -14,6 +14,11 @@
 
 namespace fa {
 
+// Placed after a lambda's parameter list: the kernels build their loop bodies from lambdas
+// that capture register arrays by reference, which only stay in registers when every call
+// is inlined.
+#define FA_INL __attribute__((always_inline))
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -42,6 +47,11 @@ struct Bf16 {
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  // acc + lo(w) + hi(w) in one instruction (v_dot2c_f32_bf16 against (1, 1)).
+  static __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+  }
 };
 
 struct F16 {
@@ -58,6 +68,11 @@ struct F16 {
   }
   static __device__ __forceinline__ float hi(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  // acc + lo(w) + hi(w) in one instruction (v_dot2c_f32_f16 against (1, 1)).
+  static __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
   }
 };
 

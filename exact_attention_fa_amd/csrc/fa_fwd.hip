@@ -29,9 +29,7 @@ namespace fa {
 
 namespace {
 
-constexpr int kFwdBR = 128;  // query rows per workgroup
 constexpr int kFwdBC = 64;   // keys per K/V tile
-constexpr int kThreads = 256;
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 of the largest probability)
 
 // Work units of the softmax of one tile, in dependency order, spread over the MFMA steps
@@ -48,17 +46,17 @@ constexpr int sm_step(int u, int nsteps) {
   return before * nsteps / total;  // the step in whose share the unit starts
 }
 
-template <typename TR, int HD, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 2)
+template <typename TR, int HD, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW)
 fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
            const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
            int Hq, int Hkv, int N, int n_qt, float c2, float scale) {
-  constexpr int BR = kFwdBR, BC = kFwdBC;
+  constexpr int BR = NW * 32, BC = kFwdBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps of S^T over the head dim
   constexpr int DB = HD / 32;               // 32-row blocks of O^T
   constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
-  constexpr int TI = TILE / 1024 / 4;       // 1 KB direct loads per wave per tile
-  static_assert(TI * 4096 == TILE, "tile must split into 1 KB loads over 4 waves");
+  constexpr int TI = TILE / 1024 / NW;      // 1 KB direct loads per wave per tile
+  static_assert(TI * 1024 * NW == TILE, "tile must split into 1 KB loads over the waves");
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2], V[2]
   char* const sK = smem;
@@ -100,7 +98,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     sl_pos_to_rc<BC>((uint32_t)((wave * TI + r) * 64 + lane), row, col);
     doff[r] = (uint32_t)(row * HD + col) * 2u;
   }
-  auto issue = [&](BufRes res, int t, char* dst) {
+  auto issue = [&](BufRes res, int t, char* dst) FA_INL {
 #pragma unroll
     for (int r = 0; r < TI; ++r) dma_to_lds<16>(res, doff[r], (uint32_t)t * (BC * HD * 2), dst + (wave * TI + r) * 1024);
   };
@@ -129,18 +127,18 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   //      share of the VALU work, so the two pipes stay interleaved.
   constexpr int RD = 4;
   // K fragment of S-step i (i = kk*2 + kb): key rows kb*32.., head-dim k-step kk.
-  auto kfrag = [&](const char* tK, int i) {
+  auto kfrag = [&](const char* tK, int i) FA_INL {
     const int kk = i >> 1, kb = i & 1;
     return lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]);
   };
   // V^T fragment of PV-step i (i = db*4 + kb*2 + t2).
-  auto vfrag = [&](const char* tV, int i) {
+  auto vfrag = [&](const char* tV, int i) FA_INL {
     const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
     return lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl);
   };
   // S^T_j = K_j Q^T (register i of block kb holds key j*BC + kb*32 + (i/8)*16 + g*8 + i%8),
   // with valu(i) run under S-step i.
-  auto scores = [&](const char* __restrict__ tK, f32x16 (&s)[2], auto&& valu) {
+  auto scores = [&](const char* __restrict__ tK, f32x16 (&s)[2], auto&& valu) FA_INL {
     constexpr int NS = 2 * KST;
     u32x4 ring[RD + 1];
 #pragma unroll
@@ -156,7 +154,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   // O^T += V^T P^T (A = V^T: rows d, k = keys, read transposed from the V tile), with
   // valu(i) run under PV-step i.
-  auto pv = [&](const char* __restrict__ tV, const u32x4 (&pb)[2][2], auto&& valu) {
+  auto pv = [&](const char* __restrict__ tV, const u32x4 (&pb)[2][2], auto&& valu) FA_INL {
     constexpr int NS = DB * 4;
     u32x4 ring[RD + 1];
 #pragma unroll
@@ -173,7 +171,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Masks, needed only on a wave's last tile (the ragged end of the keys, or the tile that
   // holds this wave's diagonal): masked scores become -inf, so exp2 (with c2 > 0) makes
   // exact zeros.
-  auto mask = [&](int j, f32x16 (&s)[2]) {
+  auto mask = [&](int j, f32x16 (&s)[2]) FA_INL {
     const int kv0 = j * BC;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -192,14 +190,14 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   bool need = false;  // uniform: O must be scaled by alpha before the next P V
   float alpha = 1.f;
   float mx0 = 0.f, mx1 = 0.f, mb = 0.f;
-  auto softmax_unit = [&](f32x16 (&s)[2], int u) {
-    if (u < kSmMax) {  // two running maxima, one per 32-key block, three-way max each
+  auto softmax_unit = [&](f32x16 (&s)[2], int u) FA_INL {
+    if (u < kSmMax) {  // two running maxima, one per 32-key block, one v_max3 each step
       const int kb = u >> 3, e = (u & 7) * 2;
       float& m = kb ? mx1 : mx0;
       if ((u & 7) == 0)
         m = fmaxf(s[kb][0], s[kb][1]);
       else
-        m = fmaxf(m, fmaxf(s[kb][e], s[kb][e + 1]));
+        m = fmaxf(fmaxf(m, s[kb][e]), s[kb][e + 1]);
     } else if (u == kSmRed) {
       const float mx = pair_max(fmaxf(mx0, mx1));
       const float m_new = fmaxf(m_run, mx);  // finite: key 0 is visible to every row
@@ -213,17 +211,23 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       s[kb][i] = fast_exp2(fmaf(s[kb][i], c2, -mb));
     }
   };
-  auto softmax_all = [&](f32x16 (&s)[2]) {
+  auto softmax_all = [&](f32x16 (&s)[2]) FA_INL {
 #pragma unroll
     for (int u = 0; u < kSmUnits; ++u) softmax_unit(s, u);
   };
   // P^T operands (slot j of (kb, t2) = P for key kb*32 + t2*16 + g*8 + j) and the row sum,
   // as 16 units: unit i packs pair i%4 of operand (i/8, (i/4)%2) and adds its two values.
+  // fp16 sums the rounded pair in one dot2 (relative rounding 2^-12, far inside the LSE
+  // tolerance even for a row with one visible key); bf16 rounding (2^-9) is not, so bf16
+  // sums the fp32 values.
   float rs = 0.f;
-  auto pack_unit = [&](u32x4 (&pb)[2][2], int i) {
+  auto pack_unit = [&](u32x4 (&pb)[2][2], int i) FA_INL {
     const int kb = i >> 3, t2 = (i >> 2) & 1, pr = i & 3, e = t2 * 8 + pr * 2;
     pb[kb][t2][pr] = TR::pack(p[kb][e], p[kb][e + 1]);
-    rs += p[kb][e] + p[kb][e + 1];
+    if constexpr (std::is_same<TR, F16>::value)
+      rs = TR::add_pair(pb[kb][t2][pr], rs);
+    else
+      rs += p[kb][e] + p[kb][e + 1];
   };
 
   // Pipeline step j (0 <= j <= T), one per K/V tile plus a drain: waits for K_j and V_{j-1},
@@ -232,7 +236,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // can tell these reads from the direct loads in flight and does not make them wait.
   enum Kind { kFirst, kFirstMasked, kSteady, kSteadyMasked, kDrain, kIdle };
   auto step = [&](auto kind_tag, const int j, char* __restrict__ nK, char* __restrict__ nV,
-                  const char* __restrict__ tK, const char* __restrict__ tV) {
+                  const char* __restrict__ tK, const char* __restrict__ tV) FA_INL {
     constexpr Kind KIND = decltype(kind_tag)::value;
     wait_vmcnt<0>();  // this wave's loads of K_j and V_{j-1} have landed
     lds_barrier();    // ... and everyone's; everyone is also done with step j-1's buffers
@@ -249,13 +253,13 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       f32x16 s[2] = {f32x16{}, f32x16{}};
       u32x4 pb[2][2];
       rs = 0.f;
-      scores(tK, s, [&](int i) {
+      scores(tK, s, [&](int i) FA_INL {
 #pragma unroll
         for (int u = i * 16 / (2 * KST); u < (i + 1) * 16 / (2 * KST); ++u) pack_unit(pb, u);
       });
       l_run += rs;
       if constexpr (KIND == kSteadyMasked) mask(j, s);
-      pv(tV, pb, [&](int i) {
+      pv(tV, pb, [&](int i) FA_INL {
 #pragma unroll
         for (int u = 0; u < kSmUnits; ++u)
           if (sm_step(u, DB * 4) == i) softmax_unit(s, u);
@@ -264,7 +268,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       p[1] = s[1];
     } else if constexpr (KIND == kFirst || KIND == kFirstMasked) {
       f32x16 s[2] = {f32x16{}, f32x16{}};
-      scores(tK, s, [](int) {});
+      scores(tK, s, [](int) FA_INL {});
       if constexpr (KIND == kFirstMasked) mask(j, s);
       softmax_all(s);
       need = false;  // O is still zero
@@ -276,7 +280,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int i = 0; i < 16; ++i) pack_unit(pb, i);
       l_run += rs;
-      pv(tV, pb, [](int) {});
+      pv(tV, pb, [](int) FA_INL {});
     }
   };
 
@@ -286,7 +290,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   char* kn = sK + TILE;
   char* vc = sV;
   char* vp = sV + TILE;
-  auto run = [&](auto kind_tag, int j) {
+  auto run = [&](auto kind_tag, int j) FA_INL {
     step(kind_tag, j, kn, vc, kc, vp);
     char* t;
     t = kc, kc = kn, kn = t;
@@ -335,18 +339,26 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-template <typename TR, int HD, bool CAUSAL>
-hipError_t launch_fwd_t(const FwdArgs& a) {
-  const int n_qt = (int)((a.N + kFwdBR - 1) / kFwdBR);
+template <typename TR, int HD, bool CAUSAL, int NW>
+hipError_t launch_fwd_nw(const FwdArgs& a) {
+  const int n_qt = (int)((a.N + NW * 32 - 1) / (NW * 32));
   const long long blocks = a.B * a.Hq * (long long)n_qt;
   // c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
   // becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
   const float c2 = a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f;
-  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
                      (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale);
   return hipGetLastError();
+}
+
+// 256-query workgroups (8 waves, one workgroup per CU) halve the K/V traffic from L2 per
+// query; small grids keep 128-query workgroups (4 waves, two per CU) to fill the 256 CUs.
+template <typename TR, int HD, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdArgs& a) {
+  const long long big = a.B * a.Hq * ((a.N + 255) / 256);
+  return big >= 512 ? launch_fwd_nw<TR, HD, CAUSAL, 8>(a) : launch_fwd_nw<TR, HD, CAUSAL, 4>(a);
 }
 
 template <typename TR>

@@ -63,6 +63,25 @@ def test_small_full(dims, dtype, causal):
     full_check(shape, seed=zlib.crc32(repr((dims, dtype, causal)).encode()) % (1 << 31))
 
 
+# Grids large enough for the 256-query forward workgroups (B*Hq*ceil(N/256) >= 512), with
+# ragged sequence ends, compared element by element.
+LARGE_GRID = [
+    (4, 32, 8, 1000, 128, "bf16", False),
+    (4, 32, 32, 777, 64, "fp16", True),
+    (2, 64, 16, 1030, 128, "fp16", True),
+]
+
+
+@pytest.mark.parametrize("dims", LARGE_GRID, ids=[f"B{b}H{hq}/{hk}N{n}D{d}{t}{'c' if cz else ''}"
+                                                  for b, hq, hk, n, d, t, cz in LARGE_GRID])
+def test_large_grid_full(dims):
+    from parity_util import full_check
+    B, Hq, Hkv, N, D, dtype, causal = dims
+    shape = Shape(B, Hq, Hkv, N, D, dtype, causal)
+    log("large grid", shape)
+    full_check(shape, seed=zlib.crc32(repr(dims).encode()) % (1 << 31))
+
+
 def test_nondefault_scale_full():
     from parity_util import full_check
     for scale in (0.0, 0.05, 0.4):
