@@ -34,7 +34,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBwdBKV = 128;  // keys per workgroup (32 per wave)
 constexpr int kBwdBQ = 64;    // query rows per streamed tile
-constexpr int kDqBR = 128;    // dQ kernel: query rows per workgroup (32 per wave)
 constexpr int kDqBC = 32;     // dQ kernel: keys per K/V tile
 
 // ---------------------------------------------------------------- preprocess
@@ -354,7 +353,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // ---------------------------------------------------------------- dQ
-// Query-stationary: a workgroup owns 128 query rows (32 per wave) of one head and streams
+// Query-stationary: a workgroup owns 128 or 256 query rows (32 per wave) of one head and streams
 // 32-key tiles of K and V of its KV head through LDS (direct loads issued three tiles ahead;
 // four K buffers, three V buffers; one barrier per tile).  Per tile j, per wave:
 //   S^T = K Q^T and dP^T = V dO^T  (K, V rows from LDS; Q and dO fragments in registers)
@@ -365,18 +364,18 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // dP^T of tile j+1, then the dQ MFMAs of tile j follow.  Keys past the end read as zero rows
 // of K and V, so their dS^T K terms vanish; only the causal diagonal needs masks.  Every dQ
 // element is produced by exactly one lane: no atomics, bitwise deterministic.
-template <typename TR, int HD, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 2)
+template <typename TR, int HD, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
               int Hq, int Hkv, int N, int n_qt, float c2, float scale) {
-  constexpr int BR = kDqBR, BC = kDqBC;
+  constexpr int BR = NW * 32, BC = kDqBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps over the head dim
   constexpr int DB = HD / 32;               // 32-row blocks of dQ^T
   constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
-  constexpr int TI = TILE / 1024 / 4;       // 1 KB direct loads per wave per tile
-  static_assert(TI * 4096 == TILE, "tile must split into 1 KB loads over 4 waves");
+  constexpr int TI = TILE / 1024 / NW;      // 1 KB direct loads per wave per tile
+  static_assert(TI * 1024 * NW == TILE, "tile must split into 1 KB loads over the waves");
   constexpr int NK = 4, NV = 3;             // K tiles j..j+3, V tiles j+1..j+3
   constexpr int RD = 4;                     // LDS operand reads issued this many MFMAs ahead
 
@@ -679,18 +678,29 @@ hipError_t dkdv_hd(const BwdArgs& a) {
   return partial ? dkdv_t<TR, HD, false, true>(a) : dkdv_t<TR, HD, false, false>(a);
 }
 
-template <typename TR, int HD, bool CAUSAL>
-hipError_t dq_t(const BwdArgs& a) {
+template <typename TR, int HD, bool CAUSAL, int NW>
+hipError_t dq_nw(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
-  const int n_qt = (int)((a.N + kDqBR - 1) / kDqBR);
+  const int n_qt = (int)((a.N + NW * 32 - 1) / (NW * 32));
   const long long blocks = a.B * a.Hq * (long long)n_qt;
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dq), (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, exp2_factor(a.scale),
                      a.scale);
   return hipGetLastError();
+}
+
+// 256-query workgroups (8 waves, one workgroup per CU) halve the K/V traffic from L2 per
+// query, which lowers the power the pass draws and lets the clock rise; D = 64 tiles are too
+// small to split over 8 waves, and small grids keep 128-query workgroups to fill the CUs.
+template <typename TR, int HD, bool CAUSAL>
+hipError_t dq_t(const BwdArgs& a) {
+  const long long big = a.B * a.Hq * ((a.N + 255) / 256);
+  if constexpr (HD == 128)
+    if (big >= 512) return dq_nw<TR, HD, CAUSAL, 8>(a);
+  return dq_nw<TR, HD, CAUSAL, 4>(a);
 }
 
 template <typename TR>

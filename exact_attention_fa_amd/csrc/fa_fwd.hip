@@ -58,9 +58,13 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int TI = TILE / 1024 / NW;      // 1 KB direct loads per wave per tile
   static_assert(TI * 1024 * NW == TILE, "tile must split into 1 KB loads over the waves");
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K[2], V[2]
+  // K/V tiles are loaded DIST steps ahead into NB = DIST + 1 buffers each.  One 8-wave
+  // workgroup per CU has LDS to spare for two steps of lead; two 4-wave workgroups share a
+  // CU and keep one.
+  constexpr int DIST = NW == 8 ? 2 : 1, NB = DIST + 1;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NB * TILE];  // K[NB], V[NB]
   char* const sK = smem;
-  char* const sV = smem + 2 * TILE;
+  char* const sV = smem + NB * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,6 +107,10 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int r = 0; r < TI; ++r) dma_to_lds<16>(res, doff[r], (uint32_t)t * (BC * HD * 2), dst + (wave * TI + r) * 1024);
   };
   issue(rK, 0, sK);
+  if constexpr (DIST == 2) {
+    if (1 < T) issue(rK, 1, sK + TILE);
+    issue(rV, 0, sV);
+  }
 
   // Q fragments: B operand of S^T = K Q^T (slot j of k-step kk = Q[qi][kk*16 + g*8 + j]).
   u32x4 qf[KST];
@@ -231,22 +239,33 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // Pipeline step j (0 <= j <= T), one per K/V tile plus a drain: waits for K_j and V_{j-1},
-  // loads K_{j+1} and V_j, then (by the kind of step) computes S_j and its softmax and/or
-  // P_{j-1} V_{j-1}.  The LDS buffers are restrict-qualified parameters so that the compiler
-  // can tell these reads from the direct loads in flight and does not make them wait.
+  // loads K_{j+DIST} and V_{j+DIST-1}, then (by the kind of step) computes S_j and its softmax
+  // and/or P_{j-1} V_{j-1}.  The LDS buffers are restrict-qualified parameters so that the
+  // compiler can tell these reads from the direct loads in flight and does not make them wait.
   enum Kind { kFirst, kFirstMasked, kSteady, kSteadyMasked, kDrain, kIdle };
   auto step = [&](auto kind_tag, const int j, char* __restrict__ nK, char* __restrict__ nV,
                   const char* __restrict__ tK, const char* __restrict__ tV) FA_INL {
     constexpr Kind KIND = decltype(kind_tag)::value;
-    wait_vmcnt<0>();  // this wave's loads of K_j and V_{j-1} have landed
-    lds_barrier();    // ... and everyone's; everyone is also done with step j-1's buffers
+    // this wave's loads of K_j and V_{j-1} have landed (the loads of the following DIST - 1
+    // steps may stay in flight: loads retire in issue order) ...
+    if constexpr (DIST == 2) {
+      if (j + 1 < T)
+        wait_vmcnt<2 * TI>();
+      else if (j < T)
+        wait_vmcnt<TI>();
+      else
+        wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // ... and everyone's; everyone is also done with step j-1's buffers
     if (need) {       // the max moved in the previous step: rescale O (rare)
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       need = false;
     }
-    if (j + 1 < T) issue(rK, j + 1, nK);
-    if (j < T) issue(rV, j, nV);
+    if (j + DIST < T) issue(rK, j + DIST, nK);
+    if (j + DIST - 1 < T) issue(rV, j + DIST - 1, nV);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (KIND == kSteady || KIND == kSteadyMasked) {
       // [S_j MFMAs | pack P_{j-1}]  [P_{j-1} V_{j-1} MFMAs | softmax of S_j]
@@ -284,17 +303,24 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // Buffers: step j reads K_j from kc and V_{j-1} from vp, and fills kn with K_{j+1} and vc
-  // with V_j; then the roles swap.
+  // Buffer rings: step j reads K_j from kc and V_{j-1} from vp and fills kd with K_{j+DIST}
+  // and vd with V_{j+DIST-1}; with DIST = 2, kf holds K_{j+1} and vf holds V_j in flight.
   char* kc = sK;
-  char* kn = sK + TILE;
-  char* vc = sV;
-  char* vp = sV + TILE;
+  char* kf = sK + TILE;
+  char* kd = sK + (NB - 1) * TILE;
+  char* vp = sV + (NB - 1) * TILE;
+  char* vf = sV;
+  char* vd = sV + (DIST - 1) * TILE;
   auto run = [&](auto kind_tag, int j) FA_INL {
-    step(kind_tag, j, kn, vc, kc, vp);
+    step(kind_tag, j, kd, vd, kc, vp);
     char* t;
-    t = kc, kc = kn, kn = t;
-    t = vc, vc = vp, vp = t;
+    if constexpr (DIST == 2) {
+      t = kc, kc = kf, kf = kd, kd = t;
+      t = vp, vp = vf, vf = vd, vd = t;
+    } else {
+      t = kc, kc = kd, kd = t;
+      t = vp, vp = vd, vd = t;
+    }
   };
   using KFirst = std::integral_constant<Kind, kFirst>;
   using KFirstMasked = std::integral_constant<Kind, kFirstMasked>;
