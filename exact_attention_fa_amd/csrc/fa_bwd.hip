@@ -176,7 +176,10 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
+    for (int i = 0; i < RD; ++i) {
+      ring[i] = frag(i);  // in use order, so each wait is partial
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < 2 * KST; ++i) {
       if (i + RD < 2 * KST) ring[(i + RD) % (RD + 1)] = frag(i + RD);
@@ -244,7 +247,10 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
+    for (int i = 0; i < RD; ++i) {
+      ring[i] = frag(i);  // in use order, so each wait is partial
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
       if (i + RD < 4 * DB) ring[(i + RD) % (RD + 1)] = frag(i + RD);
@@ -458,7 +464,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
+    for (int i = 0; i < RD; ++i) {
+      ring[i] = frag(i);  // in use order, so each wait is partial
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < 2 * KST; ++i) {
       if (i + RD < 2 * KST) ring[(i + RD) % (RD + 1)] = frag(i + RD);
@@ -495,7 +504,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int NS = 2 * DB;
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) ring[i] = frag(i);
+    for (int i = 0; i < RD; ++i) {
+      ring[i] = frag(i);  // in use order, so each wait is partial
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (i + RD < NS) ring[(i + RD) % (RD + 1)] = frag(i + RD);

@@ -37,13 +37,14 @@ constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 of the larg
 // reduction and reference update (weight 4), 32 fused scale-subtract + exp2 (weight 3 each).
 constexpr int kSmMax = 16, kSmRed = 16, kSmExp0 = 17, kSmUnits = 49;
 constexpr int sm_weight(int u) { return u < kSmMax ? 1 : (u == kSmRed ? 4 : 3); }
-constexpr int sm_step(int u, int nsteps) {
+// Step (of nsteps) in whose share unit u >= first starts, for units [first, kSmUnits).
+constexpr int sm_step(int u, int nsteps, int first) {
   int before = 0, total = 0;
-  for (int v = 0; v < kSmUnits; ++v) {
+  for (int v = first; v < kSmUnits; ++v) {
     if (v < u) before += sm_weight(v);
     total += sm_weight(v);
   }
-  return before * nsteps / total;  // the step in whose share the unit starts
+  return before * nsteps / total;
 }
 
 template <typename TR, int HD, bool CAUSAL, int NW>
@@ -134,9 +135,11 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   //      step is fenced together with the LDS read of the operand RD steps ahead and a fixed
   //      share of the VALU work, so the two pipes stay interleaved.
   constexpr int RD = 4;
-  // K fragment of S-step i (i = kk*2 + kb): key rows kb*32.., head-dim k-step kk.
+  // K fragment of S-step i (i = kb*KST + kk): key rows kb*32.., head-dim k-step kk.  The
+  // first 32-key block is finished half way through, so its row max can start under the
+  // MFMAs of the second block.
   auto kfrag = [&](const char* tK, int i) FA_INL {
-    const int kk = i >> 1, kb = i & 1;
+    const int kk = i % KST, kb = i / KST;
     return lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]);
   };
   // V^T fragment of PV-step i (i = db*4 + kb*2 + t2).
@@ -150,12 +153,15 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int NS = 2 * KST;
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) ring[i] = kfrag(tK, i);
+    for (int i = 0; i < RD; ++i) {
+      ring[i] = kfrag(tK, i);  // in use order, so each wait is partial
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (i + RD < NS) ring[(i + RD) % (RD + 1)] = kfrag(tK, i + RD);
       __builtin_amdgcn_sched_barrier(0);
-      s[i & 1] = TR::mfma(ring[i % (RD + 1)], qf[i >> 1], s[i & 1]);
+      s[i / KST] = TR::mfma(ring[i % (RD + 1)], qf[i % KST], s[i / KST]);
       valu(i);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -166,7 +172,10 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int NS = DB * 4;
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) ring[i] = vfrag(tV, i);
+    for (int i = 0; i < RD; ++i) {
+      ring[i] = vfrag(tV, i);  // in use order, so each wait is partial
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (i + RD < NS) ring[(i + RD) % (RD + 1)] = vfrag(tV, i + RD);
@@ -272,16 +281,22 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       f32x16 s[2] = {f32x16{}, f32x16{}};
       u32x4 pb[2][2];
       rs = 0.f;
+      // Without masks, the first block's maxima (units 0..7) run in the second half of the
+      // S MFMAs; a masked tile takes all of them after the mask.
+      constexpr int NS = 2 * KST, EARLY = (KIND == kSteady) ? 8 : 0;
       scores(tK, s, [&](int i) FA_INL {
 #pragma unroll
-        for (int u = i * 16 / (2 * KST); u < (i + 1) * 16 / (2 * KST); ++u) pack_unit(pb, u);
+        for (int u = i * 16 / NS; u < (i + 1) * 16 / NS; ++u) pack_unit(pb, u);
+#pragma unroll
+        for (int u = 0; u < EARLY; ++u)
+          if (KST + 1 + u * (NS - KST - 1) / EARLY == i) softmax_unit(s, u);
       });
       l_run += rs;
       if constexpr (KIND == kSteadyMasked) mask(j, s);
       pv(tV, pb, [&](int i) FA_INL {
 #pragma unroll
-        for (int u = 0; u < kSmUnits; ++u)
-          if (sm_step(u, DB * 4) == i) softmax_unit(s, u);
+        for (int u = EARLY; u < kSmUnits; ++u)
+          if (sm_step(u, DB * 4, EARLY) == i) softmax_unit(s, u);
       });
       p[0] = s[0];
       p[1] = s[1];
