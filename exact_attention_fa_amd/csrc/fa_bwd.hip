@@ -81,7 +81,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
                 uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int Hq, int Hkv,
-                int N, int n_kt, float c2, float scale) {
+                int N, int n_kt, float c2, float scale, int snake) {
   constexpr int BKV = kBwdBKV, BQ = kBwdBQ;
   constexpr int KST = HD / 16, DB = HD / 32;
   constexpr int QT_BYTES = BQ * HD * 2;
@@ -101,7 +101,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int c = lane & 31, g = lane >> 5;
 
   const int job = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = job % n_kt;  // causal: low kt has the most query tiles and comes first
+  // causal: low kt has the most query tiles
+  const int kt = CAUSAL ? n_kt - 1 - causal_tile(job % n_kt, job / n_kt, n_kt, snake) : job % n_kt;
   const int bh = job / n_kt;
   const int hq = bh % Hq, b = bh / Hq;
   const int hkv = hq / (Hq / Hkv);
@@ -375,7 +376,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
-              int Hq, int Hkv, int N, int n_qt, float c2, float scale) {
+              int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake) {
   constexpr int BR = NW * 32, BC = kDqBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps over the head dim
   constexpr int DB = HD / 32;               // 32-row blocks of dQ^T
@@ -395,7 +396,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int job = xcd_remap(blockIdx.x, gridDim.x);
   int qt = job % n_qt;
   const int bh = job / n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  if (CAUSAL) qt = causal_tile(qt, bh, n_qt, snake);
   const int hq = bh % Hq, b = bh / Hq;
   const int hkv = hq / (Hq / Hkv);
   const uint16_t* const Kh = K + ((size_t)b * Hkv + hkv) * N * HD;
@@ -679,7 +680,7 @@ hipError_t dkdv_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dkp, dvp, (int)a.Hq, (int)a.Hkv,
-                     (int)a.N, n_kt, exp2_factor(a.scale), a.scale);
+                     (int)a.N, n_kt, exp2_factor(a.scale), a.scale, (int)grid_fits(blocks, 1));
   return hipGetLastError();
 }
 
@@ -700,7 +701,7 @@ hipError_t dq_nw(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dq), (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, exp2_factor(a.scale),
-                     a.scale);
+                     a.scale, (int)grid_fits(blocks, 8 / NW));
   return hipGetLastError();
 }
 

@@ -98,6 +98,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Order of a head's causal tiles (work grows linearly with the tile index).  idx counts the
+// head's jobs in dispatch order.  When the whole grid is resident at once (`snake`),
+// consecutive heads alternate heaviest-first and lightest-first, so the two workgroups a CU
+// receives from consecutive heads add up to about the same work on every CU.  Otherwise the
+// grid runs in several rounds and heaviest-first lets the dispatcher balance as slots free up.
+__device__ __forceinline__ int causal_tile(int idx, int head, int n, int snake) {
+  return (snake && (head & 1)) ? idx : n - 1 - idx;
+}
+// Whole grid resident at once: every workgroup has a slot on some CU from the start.
+inline bool grid_fits(long long blocks, int per_cu) { return blocks <= 256LL * per_cu; }
+
 // ---------------------------------------------------------------- LDS tiles
 //
 // A tile of R rows x W 16-bit columns (W = 64 or 128) is stored as W/32 "slices" of

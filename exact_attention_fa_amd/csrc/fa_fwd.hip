@@ -51,7 +51,7 @@ template <typename TR, int HD, bool CAUSAL, int NW>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
            const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-           int Hq, int Hkv, int N, int n_qt, float c2, float scale) {
+           int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake) {
   constexpr int BR = NW * 32, BC = kFwdBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps of S^T over the head dim
   constexpr int DB = HD / 32;               // 32-row blocks of O^T
@@ -75,7 +75,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int job = xcd_remap(blockIdx.x, gridDim.x);
   int qt = job % n_qt;
   const int bh = job / n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // heaviest query tiles first
+  if (CAUSAL) qt = causal_tile(qt, bh, n_qt, snake);
   const int hq = bh % Hq, b = bh / Hq;
   const int hkv = hq / (Hq / Hkv);
   const uint16_t* const Qh = Q + (size_t)bh * N * HD;
@@ -390,7 +390,7 @@ hipError_t launch_fwd_nw(const FwdArgs& a) {
   hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale);
+                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale, (int)grid_fits(blocks, 8 / NW));
   return hipGetLastError();
 }
 
