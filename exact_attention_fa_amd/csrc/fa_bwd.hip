@@ -532,7 +532,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       wait_vmcnt<2 * TI>();
     else
       wait_vmcnt<0>();
-    lds_barrier();
+    dma_barrier();
     if (j + 3 < T) issue(j + 3, dK_, dV_);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 dsb[2];
@@ -586,7 +586,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     wait_vmcnt<2 * TI>();
   else
     wait_vmcnt<0>();
-  lds_barrier();
+  dma_barrier();
   if (Tw > 0) {
     sa = f32x16{};
     dpa = f32x16{};

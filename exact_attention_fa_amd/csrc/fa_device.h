@@ -252,6 +252,14 @@ __device__ __forceinline__ void lds_store_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Workgroup barrier for tiles filled by direct loads.  The caller has already waited (vmcnt)
+// for its own share of the tile it needs next; this drains the wave's LDS reads (so that a
+// buffer may be refilled after the barrier) and synchronises, without also waiting for direct
+// loads still in flight for later tiles, which an LDS-scoped fence would do.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt vmcnt(N): wait until at most N of this wave's vector-memory operations are
 // outstanding.  On gfx9-family targets loads, stores, atomics and direct-to-LDS loads share
 // this counter and retire in issue order.
