@@ -371,26 +371,33 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // dP^T of tile j+1, then the dQ MFMAs of tile j follow.  Keys past the end read as zero rows
 // of K and V, so their dS^T K terms vanish; only the causal diagonal needs masks.  Every dQ
 // element is produced by exactly one lane: no atomics, bitwise deterministic.
-template <typename TR, int HD, bool CAUSAL, int NW>
+// SPLIT = 2: two wave groups own the same query rows and take the two halves of the key range,
+// each with its own LDS buffers; group 1 hands its dQ^T partial to group 0 through LDS at the
+// end (one fixed-order addition, still deterministic).
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
               int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake) {
-  constexpr int BR = NW * 32, BC = kDqBC;  // query rows per workgroup (32 per wave), keys per tile
+  static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
+  constexpr int GW = NW / SPLIT;            // waves per group
+  constexpr int BR = GW * 32, BC = kDqBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps over the head dim
   constexpr int DB = HD / 32;               // 32-row blocks of dQ^T
   constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
-  constexpr int TI = TILE / 1024 / NW;      // 1 KB direct loads per wave per tile
-  static_assert(TI * 1024 * NW == TILE, "tile must split into 1 KB loads over the waves");
+  constexpr int TI = TILE / 1024 / GW;      // 1 KB direct loads per wave per tile
+  static_assert(TI * 1024 * GW == TILE, "tile must split into 1 KB loads over the waves");
   constexpr int NK = 4, NV = 3;             // K tiles j..j+3, V tiles j+1..j+3
   constexpr int RD = 4;                     // LDS operand reads issued this many MFMAs ahead
 
-  __shared__ __attribute__((aligned(1024))) char smem[(NK + NV) * TILE];
+  __shared__ __attribute__((aligned(1024))) char smem[SPLIT * (NK + NV) * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / GW;  // group (0 when SPLIT = 1)
+  const int wv = wave % GW;   // wave within the group
   const int c = lane & 31, g = lane >> 5;
 
   const int job = xcd_remap(blockIdx.x, gridDim.x);
@@ -402,8 +409,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* const Kh = K + ((size_t)b * Hkv + hkv) * N * HD;
   const uint16_t* const Vh = V + ((size_t)b * Hkv + hkv) * N * HD;
 
-  const int qw0 = qt * BR + wave * 32;  // first query row of this wave
-  const int qi = qw0 + c;               // the query of this lane's accumulator column
+  const int qw0 = qt * BR + wv * 32;  // first query row of this wave
+  const int qi = qw0 + c;             // the query of this lane's accumulator column
 
   // Key tiles the workgroup streams, and the prefix this wave computes on (causal waves stop
   // at the tile holding their diagonal; waves wholly past the last row compute nothing).
@@ -412,6 +419,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int Tw = T;
   if (CAUSAL) Tw = (min(N, qw0 + 32) - 1) / BC + 1;
   if (qw0 >= N) Tw = 0;
+  // This group's tiles [t0, t0 + Tg) (group 0 takes the larger half), the steps every wave
+  // takes (the larger group's tile count), and how many of the group's tiles this wave
+  // computes on; the wave's diagonal tile Tw - 1, when in the group's range, is its last.
+  const int half = SPLIT == 2 ? (T + 1) / 2 : T;
+  const int t0 = grp ? half : 0;
+  const int Tg = grp ? T - half : half;
+  const int Twg = max(0, min(Tw - t0, Tg));
 
   // Direct loads of K/V tile t (keys past the end read as zero).
   const BufRes rK = make_bufres(Kh, (uint32_t)N * HD * 2u), rV = make_bufres(Vh, (uint32_t)N * HD * 2u);
@@ -419,23 +433,23 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int r = 0; r < TI; ++r) {
     int row, col;
-    sl_pos_to_rc<BC>((uint32_t)((wave * TI + r) * 64 + lane), row, col);
+    sl_pos_to_rc<BC>((uint32_t)((wv * TI + r) * 64 + lane), row, col);
     kvo[r] = (uint32_t)(row * HD + col) * 2u;
   }
   auto issue = [&](int t, char* dK_, char* dV_) FA_INL {
 #pragma unroll
     for (int r = 0; r < TI; ++r) {
-      const int blk = wave * TI + r;
-      dma_to_lds<16>(rK, kvo[r], (uint32_t)t * (BC * HD * 2), dK_ + blk * 1024);
-      dma_to_lds<16>(rV, kvo[r], (uint32_t)t * (BC * HD * 2), dV_ + blk * 1024);
+      const int blk = wv * TI + r;
+      dma_to_lds<16>(rK, kvo[r], (uint32_t)(t0 + t) * (BC * HD * 2), dK_ + blk * 1024);
+      dma_to_lds<16>(rV, kvo[r], (uint32_t)(t0 + t) * (BC * HD * 2), dV_ + blk * 1024);
     }
   };
-  char* const kb0 = smem;                // K buffers kb0 + i*TILE, i < NK
-  char* const vb0 = smem + NK * TILE;    // V buffers vb0 + i*TILE, i < NV
-  // tiles 0, 1, 2 go to K buffers 0, 1, 2 and V buffers 0, 1, 2
+  char* const kb0 = smem + grp * ((NK + NV) * TILE);  // K buffers kb0 + i*TILE, i < NK
+  char* const vb0 = kb0 + NK * TILE;                   // V buffers vb0 + i*TILE, i < NV
+  // the group's tiles 0, 1, 2 go to K buffers 0, 1, 2 and V buffers 0, 1, 2
 #pragma unroll
   for (int t = 0; t < 3; ++t)
-    if (t < T) issue(t, kb0 + t * TILE, vb0 + t * TILE);
+    if (t < Tg) issue(t, kb0 + t * TILE, vb0 + t * TILE);
 
   // B operands: slot j of k-step kk = Q[qi][kk*16 + g*8 + j] and dO[qi][...]
   const size_t rowoff = (size_t)bh * N * HD + (size_t)qi * HD;
@@ -488,7 +502,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr bool MASKED = decltype(masked_tag)::value;
     float sv = s[i];
     if constexpr (MASKED) {
-      const int key = j * BC + (i >> 3) * 16 + g * 8 + (i & 7);
+      const int key = (t0 + j) * BC + (i >> 3) * 16 + g * 8 + (i & 7);
       if (key > qi) sv = -INFINITY;
     }
     const float ds = fast_exp2(fmaf(sv, c2, -l2)) * (dp[i] - dd);
@@ -528,12 +542,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const char* __restrict__ nV, char* __restrict__ dK_, char* __restrict__ dV_, f32x16& cs,
                   f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
     constexpr Kind KIND = decltype(kind_tag)::value;
-    if (j + 2 < T)
+    if (j + 2 < Tg)
       wait_vmcnt<2 * TI>();
     else
       wait_vmcnt<0>();
     dma_barrier();
-    if (j + 3 < T) issue(j + 3, dK_, dV_);
+    if (j + 3 < Tg) issue(j + 3, dK_, dV_);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 dsb[2];
     float dt;
@@ -580,35 +594,55 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   using KIdle = std::integral_constant<Kind, kIdle>;
 
   // prologue: tile 0 resident (tiles 1 and 2 may stay in flight), S^T/dP^T of tile 0
-  if (T > 2)
+  if (Tg > 2)
     wait_vmcnt<4 * TI>();
-  else if (T > 1)
+  else if (Tg > 1)
     wait_vmcnt<2 * TI>();
   else
     wait_vmcnt<0>();
   dma_barrier();
-  if (Tw > 0) {
+  if (Twg > 0) {
     sa = f32x16{};
     dpa = f32x16{};
     sdp(kb0, vb0, sa, dpa, [](int) FA_INL {});
   }
-  // Every wave takes exactly T steps (one barrier each); a wave's last computed tile Tw - 1
+  // Every wave takes exactly `half` steps (one barrier each); the group's last computed tile
   // is the only one that can need masks.
   int j = 0;
-  for (; j + 2 <= Tw - 1; j += 2) {
+  for (; j + 2 <= Twg - 1; j += 2) {
     run(KSteady{}, j, sa, dpa, sb, dpb);
     run(KSteady{}, j + 1, sb, dpb, sa, dpa);
   }
-  if (j < Tw - 1) {
+  if (j < Twg - 1) {
     run(KSteady{}, j, sa, dpa, sb, dpb);
     ++j;
     run(KLast{}, j, sb, dpb, sa, dpa);
     ++j;
-  } else if (j == Tw - 1) {
+  } else if (j == Twg - 1) {
     run(KLast{}, j, sa, dpa, sb, dpb);
     ++j;
   }
-  for (; j < T; ++j) run(KIdle{}, j, sa, dpa, sb, dpb);
+  for (; j < half; ++j) run(KIdle{}, j, sa, dpa, sb, dpb);
+
+  // ---- split workgroups: group 1 hands its dQ^T partial to the group-0 wave that owns the
+  // same rows, through LDS (free once every wave has passed the barrier).
+  if constexpr (SPLIT == 2) {
+    static_assert(GW * 64 * 16 * DB * 4 <= (int)sizeof(smem), "exchange must fit in the K/V buffers");
+    float* const xs = reinterpret_cast<float*>(smem) + wv * (64 * 16 * DB) + lane;
+    lds_barrier();
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[(db * 16 + i) * 64] = acc[db][i];
+    }
+    lds_barrier();
+    if (grp == 1) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] += xs[(db * 16 + i) * 64];
+  }
 
   // ---- epilogue: register i of acc[db] <-> dQ[qi][db*32 + (i/4)*8 + g*4 + i%4]
   if (qi < N) {
@@ -691,12 +725,13 @@ hipError_t dkdv_hd(const BwdArgs& a) {
   return partial ? dkdv_t<TR, HD, false, true>(a) : dkdv_t<TR, HD, false, false>(a);
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
 hipError_t dq_nw(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
-  const int n_qt = (int)((a.N + NW * 32 - 1) / (NW * 32));
+  constexpr int BR = NW / SPLIT * 32;
+  const int n_qt = (int)((a.N + BR - 1) / BR);
   const long long blocks = a.B * a.Hq * (long long)n_qt;
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
@@ -707,13 +742,16 @@ hipError_t dq_nw(const BwdArgs& a) {
 
 // 256-query workgroups (8 waves, one workgroup per CU) halve the K/V traffic from L2 per
 // query, which lowers the power the pass draws and lets the clock rise; D = 64 tiles are too
-// small to split over 8 waves, and small grids keep 128-query workgroups to fill the CUs.
+// small to split over 8 waves.  Smaller grids use 128-query tiles: 8-wave workgroups that split
+// the key range over two wave groups (causal grids, whose tiles carry uneven work, and grids
+// too small to give every CU two 4-wave workgroups), else 4-wave workgroups, two per CU.
 template <typename TR, int HD, bool CAUSAL>
 hipError_t dq_t(const BwdArgs& a) {
   const long long big = a.B * a.Hq * ((a.N + 255) / 256);
   if constexpr (HD == 128)
-    if (big >= 512) return dq_nw<TR, HD, CAUSAL, 8>(a);
-  return dq_nw<TR, HD, CAUSAL, 4>(a);
+    if (big >= 512) return dq_nw<TR, HD, CAUSAL, 8, 1>(a);
+  if (a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512) return dq_nw<TR, HD, CAUSAL, 8, 2>(a);
+  return dq_nw<TR, HD, CAUSAL, 4, 1>(a);
 }
 
 template <typename TR>

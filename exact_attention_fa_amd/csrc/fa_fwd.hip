@@ -47,30 +47,39 @@ constexpr int sm_step(int u, int nsteps, int first) {
   return before * nsteps / total;
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW>
+// SPLIT = 2: the workgroup's waves form two groups that own the same query rows and split
+// the K/V range in two contiguous halves (an on-chip split of the key range); each group runs
+// the online softmax over its half and the halves merge through LDS at the end, exactly, by
+// rescaling both to the larger running max.  Used where one query tile per workgroup leaves
+// the CUs short of waves (small grids) or unevenly loaded (causal).
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
            const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
            int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake) {
-  constexpr int BR = NW * 32, BC = kFwdBC;  // query rows per workgroup (32 per wave), keys per tile
+  static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
+  constexpr int GW = NW / SPLIT;            // waves per group
+  constexpr int BR = GW * 32, BC = kFwdBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps of S^T over the head dim
   constexpr int DB = HD / 32;               // 32-row blocks of O^T
   constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
-  constexpr int TI = TILE / 1024 / NW;      // 1 KB direct loads per wave per tile
-  static_assert(TI * 1024 * NW == TILE, "tile must split into 1 KB loads over the waves");
+  constexpr int TI = TILE / 1024 / GW;      // 1 KB direct loads per wave per tile
+  static_assert(TI * 1024 * GW == TILE, "tile must split into 1 KB loads over the waves");
 
   // K/V tiles are loaded DIST steps ahead into NB = DIST + 1 buffers each.  One 8-wave
   // workgroup per CU has LDS to spare for two steps of lead; two 4-wave workgroups share a
-  // CU and keep one.
-  constexpr int DIST = NW == 8 ? 2 : 1, NB = DIST + 1;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NB * TILE];  // K[NB], V[NB]
-  char* const sK = smem;
-  char* const sV = smem + NB * TILE;
+  // CU and keep one, and so do the two groups of a split workgroup.
+  constexpr int DIST = (NW == 8 && SPLIT == 1) ? 2 : 1, NB = DIST + 1;
+  __shared__ __attribute__((aligned(1024))) char smem[SPLIT * 2 * NB * TILE];  // per group: K[NB], V[NB]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / GW;  // group (0 when SPLIT = 1)
+  const int wv = wave % GW;   // wave within the group
   const int c = lane & 31, g = lane >> 5;
+  char* const sK = smem + grp * (2 * NB * TILE);
+  char* const sV = sK + NB * TILE;
 
   const int job = xcd_remap(blockIdx.x, gridDim.x);
   int qt = job % n_qt;
@@ -82,8 +91,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* const Kh = K + ((size_t)b * Hkv + hkv) * N * HD;
   const uint16_t* const Vh = V + ((size_t)b * Hkv + hkv) * N * HD;
 
-  const int qw0 = qt * BR + wave * 32;  // first query row of this wave
-  const int qi = qw0 + c;               // the query row this lane's column belongs to
+  const int qw0 = qt * BR + wv * 32;  // first query row of this wave
+  const int qi = qw0 + c;             // the query row this lane's column belongs to
 
   // K/V tiles the workgroup streams, and the prefix of them this wave computes on (causal
   // waves stop at their own diagonal; waves wholly past the last row compute nothing).
@@ -92,24 +101,33 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int Tw = T;
   if (CAUSAL) Tw = (min(N, qw0 + 32) - 1) / BC + 1;
   if (qw0 >= N) Tw = 0;
+  // This group's tiles [t0, t0 + Tg) (group 0 takes the larger half), the steps every wave
+  // takes (the larger group's tile count + 1, one barrier each), and the number of the
+  // group's tiles this wave computes on.  Only the wave's last tile Tw - 1 can need masks,
+  // and when it lies in a group's range it is that group's last computed tile.
+  const int half = SPLIT == 2 ? (T + 1) / 2 : T;
+  const int t0 = grp ? half : 0;
+  const int Tg = grp ? T - half : half;
+  const int Twg = max(0, min(Tw - t0, Tg));
 
-  // Direct loads of tile t of K or V into `dst` (rows past the end read as zero, which the
-  // masks then exclude).
+  // Direct loads of the group's tile t of K or V into `dst` (rows past the end read as zero,
+  // which the masks then exclude).
   const BufRes rK = make_bufres(Kh, (uint32_t)N * HD * 2u), rV = make_bufres(Vh, (uint32_t)N * HD * 2u);
   uint32_t doff[TI];
 #pragma unroll
   for (int r = 0; r < TI; ++r) {
     int row, col;
-    sl_pos_to_rc<BC>((uint32_t)((wave * TI + r) * 64 + lane), row, col);
+    sl_pos_to_rc<BC>((uint32_t)((wv * TI + r) * 64 + lane), row, col);
     doff[r] = (uint32_t)(row * HD + col) * 2u;
   }
   auto issue = [&](BufRes res, int t, char* dst) FA_INL {
 #pragma unroll
-    for (int r = 0; r < TI; ++r) dma_to_lds<16>(res, doff[r], (uint32_t)t * (BC * HD * 2), dst + (wave * TI + r) * 1024);
+    for (int r = 0; r < TI; ++r)
+      dma_to_lds<16>(res, doff[r], (uint32_t)(t0 + t) * (BC * HD * 2), dst + (wv * TI + r) * 1024);
   };
-  issue(rK, 0, sK);
+  if (0 < Tg) issue(rK, 0, sK);
   if constexpr (DIST == 2) {
-    if (1 < T) issue(rK, 1, sK + TILE);
+    if (1 < Tg) issue(rK, 1, sK + TILE);
     issue(rV, 0, sV);
   }
 
@@ -189,7 +207,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // holds this wave's diagonal): masked scores become -inf, so exp2 (with c2 > 0) makes
   // exact zeros.
   auto mask = [&](int j, f32x16 (&s)[2]) FA_INL {
-    const int kv0 = j * BC;
+    const int kv0 = (t0 + j) * BC;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -258,9 +276,9 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // this wave's loads of K_j and V_{j-1} have landed (the loads of the following DIST - 1
     // steps may stay in flight: loads retire in issue order) ...
     if constexpr (DIST == 2) {
-      if (j + 1 < T)
+      if (j + 1 < Tg)
         wait_vmcnt<2 * TI>();
-      else if (j < T)
+      else if (j < Tg)
         wait_vmcnt<TI>();
       else
         wait_vmcnt<0>();
@@ -273,8 +291,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       need = false;
     }
-    if (j + DIST < T) issue(rK, j + DIST, nK);
-    if (j + DIST - 1 < T) issue(rV, j + DIST - 1, nV);
+    if (j + DIST < Tg) issue(rK, j + DIST, nK);
+    if (j + DIST - 1 < Tg) issue(rV, j + DIST - 1, nV);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (KIND == kSteady || KIND == kSteadyMasked) {
       // [S_j MFMAs | pack P_{j-1}]  [P_{j-1} V_{j-1} MFMAs | softmax of S_j]
@@ -343,23 +361,53 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   using KSteadyMasked = std::integral_constant<Kind, kSteadyMasked>;
   using KDrain = std::integral_constant<Kind, kDrain>;
   using KIdle = std::integral_constant<Kind, kIdle>;
-  // Every wave takes exactly T + 1 steps (one barrier each); a wave's last computed tile
-  // Tw - 1 is the only one that can need masks.
-  if (Tw == 0) {
-    for (int j = 0; j <= T; ++j) run(KIdle{}, j);
+  // Every wave takes exactly half + 1 steps (one barrier each); the group's last computed
+  // tile is the only one that can need masks.
+  if (Twg == 0) {
+    for (int j = 0; j <= half; ++j) run(KIdle{}, j);
   } else {
-    if (Tw == 1)
+    if (Twg == 1)
       run(KFirstMasked{}, 0);
     else
       run(KFirst{}, 0);
-    for (int j = 1; j < Tw - 1; ++j) run(KSteady{}, j);
-    if (Tw >= 2) run(KSteadyMasked{}, Tw - 1);
-    run(KDrain{}, Tw);
-    for (int j = Tw + 1; j <= T; ++j) run(KIdle{}, j);
+    for (int j = 1; j < Twg - 1; ++j) run(KSteady{}, j);
+    if (Twg >= 2) run(KSteadyMasked{}, Twg - 1);
+    run(KDrain{}, Twg);
+    for (int j = Twg + 1; j <= half; ++j) run(KIdle{}, j);
   }
   if (need) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+  }
+
+  // ---- split workgroups: group 1 hands its (O, running max, running sum) to the group-0 wave
+  // that owns the same rows, through LDS (the K/V buffers are free once every wave has passed
+  // the barrier).  Both halves are rescaled to the larger max: exp2 of (m_h - m) * c2, which is
+  // 0 for a half that saw no key (m_h = -inf).
+  if constexpr (SPLIT == 2) {
+    constexpr int XW = 16 * DB + 2;  // floats per lane: O, max, sum
+    static_assert(GW * 64 * XW * 4 <= (int)sizeof(smem), "exchange must fit in the K/V buffers");
+    float* const xs = reinterpret_cast<float*>(smem) + wv * (64 * XW) + lane;
+    lds_barrier();
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[(db * 16 + i) * 64] = acc[db][i];
+      xs[(16 * DB) * 64] = m_run;
+      xs[(16 * DB + 1) * 64] = l_run;
+    }
+    lds_barrier();
+    if (grp == 1) return;
+    const float m1 = xs[(16 * DB) * 64], l1 = xs[(16 * DB + 1) * 64];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = fast_exp2((m_run - m) * c2), a1 = fast_exp2((m1 - m) * c2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] = acc[db][i] * a0 + xs[(db * 16 + i) * 64] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
   }
 
   // ---- epilogue: normalise, write O (input dtype, RNE) and LSE (natural log, fp32)
@@ -380,26 +428,37 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW>
+// 128-query grids that split the key range inside the workgroup: causal grids, whose tiles
+// carry uneven work, and grids too small to give every CU two 4-wave workgroups.
+inline bool fwd_split_kv(const FwdArgs& a) {
+  return a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512;
+}
+
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
 hipError_t launch_fwd_nw(const FwdArgs& a) {
-  const int n_qt = (int)((a.N + NW * 32 - 1) / (NW * 32));
+  constexpr int BR = NW / SPLIT * 32;
+  const int n_qt = (int)((a.N + BR - 1) / BR);
   const long long blocks = a.B * a.Hq * (long long)n_qt;
   // c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
   // becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
   const float c2 = a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f;
-  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                     a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
                      (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale, (int)grid_fits(blocks, 8 / NW));
   return hipGetLastError();
 }
 
 // 256-query workgroups (8 waves, one workgroup per CU) halve the K/V traffic from L2 per
-// query; small grids keep 128-query workgroups (4 waves, two per CU) to fill the 256 CUs.
+// query.  Smaller grids use 128-query tiles: as 8-wave workgroups that split the key range
+// over two wave groups (one per CU), which keeps two waves on every SIMD and evens out causal
+// work, or as 4-wave workgroups (two per CU).
 template <typename TR, int HD, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a) {
   const long long big = a.B * a.Hq * ((a.N + 255) / 256);
-  return big >= 512 ? launch_fwd_nw<TR, HD, CAUSAL, 8>(a) : launch_fwd_nw<TR, HD, CAUSAL, 4>(a);
+  if (big >= 512) return launch_fwd_nw<TR, HD, CAUSAL, 8, 1>(a);
+  if (fwd_split_kv(a)) return launch_fwd_nw<TR, HD, CAUSAL, 8, 2>(a);
+  return launch_fwd_nw<TR, HD, CAUSAL, 4, 1>(a);
 }
 
 template <typename TR>

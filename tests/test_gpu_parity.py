@@ -63,12 +63,20 @@ def test_small_full(dims, dtype, causal):
     full_check(shape, seed=zlib.crc32(repr((dims, dtype, causal)).encode()) % (1 << 31))
 
 
-# Grids large enough for the 256-query forward workgroups (B*Hq*ceil(N/256) >= 512), with
-# ragged sequence ends, compared element by element.
+# Grids large enough for the 256-query workgroups (B*Hq*ceil(N/256) >= 512), and non-causal
+# grids of 128-query tiles that fill every CU with two 4-wave workgroups
+# (B*Hq*ceil(N/128) >= 512); everything smaller, and every other causal grid, takes the
+# workgroups that split the key range over two wave groups (the small shapes above).  Ragged
+# sequence ends, compared element by element.
 LARGE_GRID = [
     (4, 32, 8, 1000, 128, "bf16", False),
     (4, 32, 32, 777, 64, "fp16", True),
     (2, 64, 16, 1030, 128, "fp16", True),
+    (2, 32, 8, 1000, 64, "fp16", False),
+    (1, 64, 64, 900, 128, "bf16", False),
+    # split key range over many tiles per group, GQA, ragged
+    (1, 8, 2, 2000, 128, "bf16", False),
+    (1, 8, 8, 1500, 64, "fp16", True),
 ]
 
 
