@@ -70,7 +70,16 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // workgroup per CU has LDS to spare for two steps of lead; two 4-wave workgroups share a
   // CU and keep one, and so do the two groups of a split workgroup.
   constexpr int DIST = (NW == 8 && SPLIT == 1) ? 2 : 1, NB = DIST + 1;
-  __shared__ __attribute__((aligned(1024))) char smem[SPLIT * 2 * NB * TILE];  // per group: K[NB], V[NB]
+  // SUMCHK: the running max is not tracked per tile.  Probabilities are formed against the
+  // reference max, and the row sum, computed anyway, bounds every one of them: while a lane's
+  // share of the tile's sum stays <= 2^7, no probability exceeds 2^8 and nothing needs to be
+  // rescaled.  Otherwise (rare: a score far above the reference) the tile's scores are
+  // recomputed from its K tile, still resident in a fourth K buffer, and handled exactly as
+  // the tracked-max path would.  This takes the 16 v_max3 and the cross-lane reduction per
+  // tile off the VALU.
+  constexpr bool SUMCHK = DIST == 2;
+  constexpr int NBK = SUMCHK ? NB + 1 : NB;
+  __shared__ __attribute__((aligned(1024))) char smem[SPLIT * (NBK + NB) * TILE];  // per group: K[NBK], V[NB]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -78,8 +87,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int grp = wave / GW;  // group (0 when SPLIT = 1)
   const int wv = wave % GW;   // wave within the group
   const int c = lane & 31, g = lane >> 5;
-  char* const sK = smem + grp * (2 * NB * TILE);
-  char* const sV = sK + NB * TILE;
+  char* const sK = smem + grp * ((NBK + NB) * TILE);
+  char* const sV = sK + NBK * TILE;
 
   const int job = xcd_remap(blockIdx.x, gridDim.x);
   int qt = job % n_qt;
@@ -270,8 +279,47 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // and/or P_{j-1} V_{j-1}.  The LDS buffers are restrict-qualified parameters so that the
   // compiler can tell these reads from the direct loads in flight and does not make them wait.
   enum Kind { kFirst, kFirstMasked, kSteady, kSteadyMasked, kDrain, kIdle };
+  // The rare path of SUMCHK: P_{jp} (the previous tile, its K tile in tKp) is recomputed with
+  // the reference moved to the tile's max; l is rescaled here and O (flagged by `need`) just
+  // before P_{jp} V_{jp} is added.
+  auto redo = [&](const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2]) FA_INL {
+    p[0] = f32x16{};
+    p[1] = f32x16{};
+    scores(tKp, p, [](int) FA_INL {});
+    mask(jp, p);  // a no-op unless jp is the wave's last tile
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, p[kb][i]);
+    const float m_new = fmaxf(m_run, pair_max(mx));
+    alpha = fast_exp2((m_run - m_new) * c2);
+    need = true;
+    l_run *= alpha;
+    m_run = m_new;
+    mb = m_run * c2;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[kb][i] = fast_exp2(fmaf(p[kb][i], c2, -mb));
+    rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pack_unit(pb, i);
+  };
+  auto check = [&](const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2]) FA_INL {
+    if constexpr (SUMCHK) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= 0x1p7f)) != 0, 0)) redo(tKp, jp, pb);
+      if (need) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        need = false;
+      }
+    }
+  };
+
   auto step = [&](auto kind_tag, const int j, char* __restrict__ nK, char* __restrict__ nV,
-                  const char* __restrict__ tK, const char* __restrict__ tV) FA_INL {
+                  const char* __restrict__ tK, const char* __restrict__ tV,
+                  const char* __restrict__ pK) FA_INL {
     constexpr Kind KIND = decltype(kind_tag)::value;
     // this wave's loads of K_j and V_{j-1} have landed (the loads of the following DIST - 1
     // steps may stay in flight: loads retire in issue order) ...
@@ -300,8 +348,10 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       u32x4 pb[2][2];
       rs = 0.f;
       // Without masks, the first block's maxima (units 0..7) run in the second half of the
-      // S MFMAs; a masked tile takes all of them after the mask.
-      constexpr int NS = 2 * KST, EARLY = (KIND == kSteady) ? 8 : 0;
+      // S MFMAs; a masked tile takes all of them after the mask.  SUMCHK runs the exp2 units
+      // only (FIRST = kSmExp0).
+      constexpr int NS = 2 * KST, EARLY = (KIND == kSteady && !SUMCHK) ? 8 : 0;
+      constexpr int FIRST = SUMCHK ? kSmExp0 : EARLY;
       scores(tK, s, [&](int i) FA_INL {
 #pragma unroll
         for (int u = i * 16 / NS; u < (i + 1) * 16 / NS; ++u) pack_unit(pb, u);
@@ -309,12 +359,13 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int u = 0; u < EARLY; ++u)
           if (KST + 1 + u * (NS - KST - 1) / EARLY == i) softmax_unit(s, u);
       });
+      check(pK, j - 1, pb);
       l_run += rs;
       if constexpr (KIND == kSteadyMasked) mask(j, s);
       pv(tV, pb, [&](int i) FA_INL {
 #pragma unroll
-        for (int u = EARLY; u < kSmUnits; ++u)
-          if (sm_step(u, DB * 4, EARLY) == i) softmax_unit(s, u);
+        for (int u = FIRST; u < kSmUnits; ++u)
+          if (sm_step(u, DB * 4, FIRST) == i) softmax_unit(s, u);
       });
       p[0] = s[0];
       p[1] = s[1];
@@ -331,23 +382,29 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       rs = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) pack_unit(pb, i);
+      check(pK, j - 1, pb);
       l_run += rs;
       pv(tV, pb, [](int) FA_INL {});
     }
   };
 
   // Buffer rings: step j reads K_j from kc and V_{j-1} from vp and fills kd with K_{j+DIST}
-  // and vd with V_{j+DIST-1}; with DIST = 2, kf holds K_{j+1} and vf holds V_j in flight.
+  // and vd with V_{j+DIST-1}; with DIST = 2, kf holds K_{j+1} and vf holds V_j in flight, and
+  // kp keeps K_{j-1} (SUMCHK).
   char* kc = sK;
   char* kf = sK + TILE;
   char* kd = sK + (NB - 1) * TILE;
+  char* kp = sK + (NBK - 1) * TILE;
   char* vp = sV + (NB - 1) * TILE;
   char* vf = sV;
   char* vd = sV + (DIST - 1) * TILE;
   auto run = [&](auto kind_tag, int j) FA_INL {
-    step(kind_tag, j, kd, vd, kc, vp);
+    step(kind_tag, j, kd, vd, kc, vp, kp);
     char* t;
-    if constexpr (DIST == 2) {
+    if constexpr (SUMCHK) {
+      t = kp, kp = kc, kc = kf, kf = kd, kd = t;
+      t = vp, vp = vf, vf = vd, vd = t;
+    } else if constexpr (DIST == 2) {
       t = kc, kc = kf, kf = kd, kd = t;
       t = vp, vp = vf, vf = vd, vd = t;
     } else {

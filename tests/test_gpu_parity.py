@@ -90,6 +90,46 @@ def test_large_grid_full(dims):
     full_check(shape, seed=zlib.crc32(repr(dims).encode()) % (1 << 31))
 
 
+# Scores that rise along the key axis, so that later key tiles far exceed the running maximum
+# set by the first tile: the forward must move its reference and rescale (including scores
+# large enough to overflow exp2 against the old reference).  The grids are large enough for
+# the 256-query workgroups.  Inputs: the seeded draw with key row j multiplied by
+# 1 + (R - 1) j / (N - 1).
+RISING = [
+    (4, 32, 8, 1000, 128, "bf16", False, 4.0),
+    (4, 32, 8, 1000, 128, "bf16", False, 40.0),
+    (2, 64, 16, 1030, 128, "fp16", True, 6.0),
+    (4, 32, 32, 777, 64, "fp16", False, 30.0),
+]
+
+
+@pytest.mark.parametrize("dims", RISING, ids=[f"B{b}H{hq}/{hk}N{n}D{d}{t}{'c' if cz else ''}R{r:g}"
+                                              for b, hq, hk, n, d, t, cz, r in RISING])
+def test_rising_scores_full(dims):
+    import numpy as np
+    import torch
+    from parity_util import (assert_fwd_close, assert_grad_close, attention_backward, attention_forward,
+                             derived_o_tol, f64, gpu_backward, gpu_forward)
+    from exact_attention_fa_amd.inputs import make_inputs
+    B, Hq, Hkv, N, D, dtype, causal, R = dims
+    shape = Shape(B, Hq, Hkv, N, D, dtype, causal)
+    log("rising scores", shape, "ramp", R)
+    q, k, v, do = make_inputs(shape, seed=zlib.crc32(repr(dims).encode()) % (1 << 31))
+    ramp = 1.0 + (R - 1.0) * torch.arange(N, dtype=torch.float32) / max(N - 1, 1)
+    k = (k.float() * ramp[None, None, :, None]).to(k.dtype)
+    o, lse = gpu_forward(q, k, v, causal, shape.scale)
+    o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v), shape.scale, causal)
+    errs = assert_fwd_close(f64(o), f64(lse), o_ref, lse_ref, str(shape), derived_o_tol(f64(v), dtype))
+    log("  fwd errors", errs)
+    assert np.isfinite(f64(o)).all()
+    if R > 8.0:
+        return  # nearly one-hot rows: the gradients are a cancellation the tolerance does not cover
+    dq, dk, dv = gpu_backward(q, k, v, o, do, lse, causal, shape.scale)
+    dq_r, dk_r, dv_r = attention_backward(f64(q), f64(k), f64(v), f64(do), shape.scale, causal)
+    for name, g, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
+        assert_grad_close(f64(g), r, name, str(shape))
+
+
 def test_nondefault_scale_full():
     from parity_util import full_check
     for scale in (0.0, 0.05, 0.4):
