@@ -77,7 +77,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // recomputed from its K tile, still resident in a fourth K buffer, and handled exactly as
   // the tracked-max path would.  This takes the 16 v_max3 and the cross-lane reduction per
   // tile off the VALU.
-  constexpr bool SUMCHK = DIST == 2;
+  constexpr bool SUMCHK = true;
   constexpr int NBK = SUMCHK ? NB + 1 : NB;
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * (NBK + NB) * TILE];  // per group: K[NBK], V[NB]
 
@@ -401,9 +401,12 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto run = [&](auto kind_tag, int j) FA_INL {
     step(kind_tag, j, kd, vd, kc, vp, kp);
     char* t;
-    if constexpr (SUMCHK) {
+    if constexpr (SUMCHK && DIST == 2) {
       t = kp, kp = kc, kc = kf, kf = kd, kd = t;
       t = vp, vp = vf, vf = vd, vd = t;
+    } else if constexpr (SUMCHK) {
+      t = kp, kp = kc, kc = kd, kd = t;
+      t = vp, vp = vd, vd = t;
     } else if constexpr (DIST == 2) {
       t = kc, kc = kf, kf = kd, kd = t;
       t = vp, vp = vf, vf = vd, vd = t;
