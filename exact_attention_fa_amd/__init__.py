@@ -21,7 +21,8 @@ import os
 import threading
 
 __all__ = [
-    "fa_fwd", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_postprocess",
+    "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_size",
+    "fa_merge_partials", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_postprocess",
     "fa_bwd_workspace_size", "fa_version", "fa_status_string", "library_path", "load_library",
     "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16",
 ]
@@ -39,6 +40,12 @@ _SIGS = {
     "fa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "fa_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float,
                 ctypes.c_int, ctypes.c_int, _vp], ctypes.c_int),
+    "fa_fwd_splitkv_parts": ([_i64, _i64, _i64, _i64, _i64, ctypes.c_int], ctypes.c_int),
+    "fa_fwd_splitkv_workspace_size": ([_i64, _i64, _i64, _i64, _i64, ctypes.c_int], ctypes.c_size_t),
+    "fa_fwd_splitkv": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, ctypes.c_int,
+                        _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
+                       ctypes.c_int),
+    "fa_merge_partials": ([_vp, _vp, ctypes.c_int, _vp, _vp, _i64, _i64, ctypes.c_int, _vp], ctypes.c_int),
     "fa_bwd_workspace_size": ([_i64, _i64, _i64, _i64, _i64], ctypes.c_size_t),
     "fa_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                 _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
@@ -132,6 +139,10 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _scale(D, softmax_scale):
     return 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
 
@@ -150,6 +161,55 @@ def fa_fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None
                                _scale(D, softmax_scale), int(bool(causal)), code, _stream(q))
     _check(rc, "fa_fwd")
     return o, l
+
+
+def fa_fwd_splitkv_parts(B, Hq, Hkv, N, D, causal: bool = False) -> int:
+    """The library's choice of key-range pieces for fa_fwd_splitkv (1: no split)."""
+    return int(load_library().fa_fwd_splitkv_parts(B, Hq, Hkv, N, D, int(bool(causal))))
+
+
+def fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, n_split: int) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, int(n_split)))
+
+
+def fa_fwd_splitkv(q, k, v, causal: bool = False, softmax_scale=None, n_split: int = 0, workspace=None,
+                   out=None, lse=None):
+    """Forward over n_split key-range pieces merged through their LSEs (0: the library's
+    choice); returns (o, lse) like fa_fwd."""
+    import torch
+    B, Hq, Hkv, N, D = _dims(q, k, v)
+    _require(q, k, v, dtype=q.dtype)
+    code = _dtype_code(q)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o, dtype=q.dtype)
+    _require(l, dtype=torch.float32)
+    n = fa_fwd_splitkv_parts(B, Hq, Hkv, N, D, causal) if n_split == 0 else int(n_split)
+    if workspace is None and 1 <= n <= 64:
+        need = fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, n)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    nbytes = 0 if workspace is None else _nbytes(workspace)
+    rc = load_library().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(workspace), nbytes,
+                                       int(n_split), B, Hq, Hkv, N, D, _scale(D, softmax_scale),
+                                       int(bool(causal)), code, _stream(q))
+    _check(rc, "fa_fwd_splitkv")
+    return o, l
+
+
+def fa_merge_partials(o_parts, lse_parts, out, lse):
+    """Merge fp32 partial results over disjoint key sets: o_parts (n, rows, D), lse_parts
+    (n, rows) -> out (rows, D) in out's dtype, lse (rows,) float32 (any shapes with these
+    element counts)."""
+    import torch
+    n = lse_parts.shape[0]
+    rows = lse_parts.numel() // n
+    D = o_parts.numel() // (n * rows)
+    _require(o_parts, lse_parts, dtype=torch.float32)
+    _require(out)
+    _require(lse, dtype=torch.float32)
+    rc = load_library().fa_merge_partials(_ptr(o_parts), _ptr(lse_parts), n, _ptr(out), _ptr(lse), rows, D,
+                                          _dtype_code(out), _stream(out))
+    _check(rc, "fa_merge_partials")
 
 
 def fa_bwd_workspace_size(B, Hq, Hkv, N, D) -> int:
@@ -191,10 +251,6 @@ def fa_bwd_preprocess(o, do, lse, workspace, Hkv: int):
                                           workspace.numel() * workspace.element_size(),
                                           B, Hq, Hkv, N, D, _dtype_code(o), _stream(o))
     _check(rc, "fa_bwd_preprocess")
-
-
-def _nbytes(t):
-    return t.numel() * t.element_size()
 
 
 def fa_bwd_dkdv(q, k, v, do, dk, dv, workspace, causal=False, softmax_scale=None):

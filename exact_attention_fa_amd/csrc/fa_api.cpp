@@ -13,7 +13,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kMaxParts = 64;    // key-range pieces / merge parts per call
 
 size_t round_up(size_t x) { return (x + 255u) & ~(size_t)255u; }
 
@@ -107,6 +108,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_TOO_LARGE: return "problem size exceeds the 32-bit index range of the kernels";
     case FA_ERR_ALIAS: return "an output buffer overlaps another buffer of the call";
+    case FA_ERR_SPLIT: return "split / part count out of range (1..64, or 0 for the library's choice)";
     default: return "unknown status";
   }
 }
@@ -128,6 +130,68 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, D, softmax_scale, causal != 0, dtype == FA_BF16,
             static_cast<hipStream_t>(stream)};
   return status_of(launch_fwd(a));
+}
+
+int fa_fwd_splitkv_parts(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int causal) {
+  if (check_dims(B, Hq, Hkv, N, D) != FA_OK) return 0;
+  return fwd_auto_parts(B, Hq, N, D, causal != 0);
+}
+
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int n_split) {
+  if (check_dims(B, Hq, Hkv, N, D) != FA_OK || n_split < 1 || n_split > kMaxParts) return 0;
+  if (n_split == 1) return 0;
+  const size_t rows = (size_t)B * (size_t)Hq * (size_t)N;
+  return round_up((size_t)n_split * rows * (size_t)D * 4) + round_up((size_t)n_split * rows * 4);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, int n_split, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                   float softmax_scale, int causal, int dtype, void* stream) {
+  FA_TRY(check_dtype(dtype));
+  FA_TRY(check_dims(B, Hq, Hkv, N, D));
+  FA_TRY(check_scale(softmax_scale));
+  if (n_split < 0 || n_split > kMaxParts) return FA_ERR_SPLIT;
+  const int n = n_split == 0 ? fwd_auto_parts(B, Hq, N, D, causal != 0) : n_split;
+  if (n == 1) return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, D, softmax_scale, causal, dtype, stream);
+  FA_TRY(check_ptr(q, 16));
+  FA_TRY(check_ptr(k, 16));
+  FA_TRY(check_ptr(v, 16));
+  FA_TRY(check_ptr(o, 16));
+  FA_TRY(check_ptr(lse, 4));
+  FA_TRY(check_ptr(workspace, 256));
+  const size_t need = fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, n);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t rows = (size_t)(B * Hq * N);
+  const size_t qb = rows * (size_t)D * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {o, qb, true}, {lse, rows * 4, true},
+                     {workspace, need, true}};
+  FA_TRY(check_alias(r, 6));
+  float* const op = static_cast<float*>(workspace);
+  float* const lp = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((size_t)n * rows * D * 4));
+  FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, D, softmax_scale, causal != 0, dtype == FA_BF16,
+            static_cast<hipStream_t>(stream), n, op, lp};
+  FA_TRY(status_of(launch_fwd(a)));
+  const MergeArgs m{op, lp, n, (long long)rows, D, o, lse, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
+  return status_of(launch_merge(m));
+}
+
+int fa_merge_partials(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int64_t rows,
+                      int64_t D, int dtype, void* stream) {
+  FA_TRY(check_dtype(dtype));
+  if (rows <= 0) return FA_ERR_BAD_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (n_parts < 1 || n_parts > kMaxParts) return FA_ERR_SPLIT;
+  if (rows > (int64_t)INT32_MAX * 8 / D) return FA_ERR_TOO_LARGE;
+  FA_TRY(check_ptr(o_parts, 16));
+  FA_TRY(check_ptr(lse_parts, 4));
+  FA_TRY(check_ptr(o, 16));
+  FA_TRY(check_ptr(lse, 4));
+  const size_t pr = (size_t)n_parts * (size_t)rows;
+  const Range r[] = {{o_parts, pr * (size_t)D * 4, false}, {lse_parts, pr * 4, false},
+                     {o, (size_t)rows * (size_t)D * 2, true}, {lse, (size_t)rows * 4, true}};
+  FA_TRY(check_alias(r, 4));
+  const MergeArgs m{o_parts, lse_parts, n_parts, rows, D, o, lse, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
+  return status_of(launch_merge(m));
 }
 
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D) {

@@ -52,11 +52,17 @@ constexpr int sm_step(int u, int nsteps, int first) {
 // the online softmax over its half and the halves merge through LDS at the end, exactly, by
 // rescaling both to the larger running max.  Used where one query tile per workgroup leaves
 // the CUs short of waves (small grids) or unevenly loaded (causal).
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
+//
+// PART: the key range of every query tile is also cut into `n_part` contiguous pieces, one
+// workgroup each, and each workgroup writes its piece's normalised output and log-sum-exp as
+// fp32 partials (Op, Lp) for a merge pass (merge_kernel).  A piece (or half) that holds no
+// visible key for a row yields O = 0 and LSE = -inf there.
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
            const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-           int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake) {
+           int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake, int n_part,
+           float* __restrict__ Op, float* __restrict__ Lp) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
   constexpr int GW = NW / SPLIT;            // waves per group
   constexpr int BR = GW * 32, BC = kFwdBC;  // query rows per workgroup (32 per wave), keys per tile
@@ -90,7 +96,12 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   char* const sK = smem + grp * ((NBK + NB) * TILE);
   char* const sV = sK + NBK * TILE;
 
-  const int job = xcd_remap(blockIdx.x, gridDim.x);
+  int job = xcd_remap(blockIdx.x, gridDim.x);
+  int part = 0;  // piece of the key range (PART)
+  if constexpr (PART) {
+    part = job % n_part;
+    job /= n_part;
+  }
   int qt = job % n_qt;
   const int bh = job / n_qt;
   if (CAUSAL) qt = causal_tile(qt, bh, n_qt, snake);
@@ -114,9 +125,11 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // takes (the larger group's tile count + 1, one barrier each), and the number of the
   // group's tiles this wave computes on.  Only the wave's last tile Tw - 1 can need masks,
   // and when it lies in a group's range it is that group's last computed tile.
-  const int half = SPLIT == 2 ? (T + 1) / 2 : T;
-  const int t0 = grp ? half : 0;
-  const int Tg = grp ? T - half : half;
+  const int tb = PART ? (int)((long long)T * part / n_part) : 0;  // this workgroup's piece [tb, te)
+  const int te = PART ? (int)((long long)T * (part + 1) / n_part) : T;
+  const int half = SPLIT == 2 ? (te - tb + 1) / 2 : te - tb;
+  const int t0 = tb + (grp ? half : 0);
+  const int Tg = grp ? te - tb - half : half;
   const int Twg = max(0, min(Tw - t0, Tg));
 
   // Direct loads of the group's tile t of K or V into `dst` (rows past the end read as zero,
@@ -461,7 +474,9 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (grp == 1) return;
     const float m1 = xs[(16 * DB) * 64], l1 = xs[(16 * DB + 1) * 64];
     const float m = fmaxf(m_run, m1);
-    const float a0 = fast_exp2((m_run - m) * c2), a1 = fast_exp2((m1 - m) * c2);
+    // (equal maxima take weight 1, which also keeps two empty halves, m = -inf, NaN-free)
+    const float a0 = m_run == m ? 1.f : fast_exp2((m_run - m) * c2);
+    const float a1 = m1 == m ? 1.f : fast_exp2((m1 - m) * c2);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -472,6 +487,26 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // ---- epilogue: normalise, write O (input dtype, RNE) and LSE (natural log, fp32)
   const float l_tot = pair_sum(l_run);
+  if constexpr (PART) {
+    // fp32 partials of piece `part`; a row with no visible key in the piece: O = 0, LSE = -inf
+    if (qi < N) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const size_t rows = (size_t)(gridDim.x / (n_part * n_qt)) * N;  // B * Hq * N
+      const size_t row = (size_t)part * rows + (size_t)bh * N + qi;
+      float* const orow = Op + row * HD;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = db * 32 + i4 * 8 + g * 4;
+          const f32x4 w = {acc[db][i4 * 4 + 0] * inv, acc[db][i4 * 4 + 1] * inv, acc[db][i4 * 4 + 2] * inv,
+                           acc[db][i4 * 4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + d) = w;
+        }
+      if (g == 0) Lp[row] = l_tot > 0.f ? m_run * scale + __logf(l_tot) : -INFINITY;
+    }
+    return;
+  }
   const float inv = 1.f / l_tot;
   if (qi < N) {
     uint16_t* const orow = O + (size_t)bh * N * HD + (size_t)qi * HD;
@@ -494,18 +529,20 @@ inline bool fwd_split_kv(const FwdArgs& a) {
   return a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512;
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false>
 hipError_t launch_fwd_nw(const FwdArgs& a) {
   constexpr int BR = NW / SPLIT * 32;
   const int n_qt = (int)((a.N + BR - 1) / BR);
-  const long long blocks = a.B * a.Hq * (long long)n_qt;
+  const int n_part = PART ? a.n_part : 1;
+  const long long blocks = a.B * a.Hq * (long long)n_qt * n_part;
   // c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
   // becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
   const float c2 = a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f;
-  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW, SPLIT, PART>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale, (int)grid_fits(blocks, 8 / NW));
+                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale, (int)grid_fits(blocks, 8 / NW), n_part,
+                     a.o_part, a.lse_part);
   return hipGetLastError();
 }
 
@@ -527,10 +564,80 @@ hipError_t launch_fwd_dt(const FwdArgs& a) {
   return a.causal ? launch_fwd_t<TR, 128, true>(a) : launch_fwd_t<TR, 128, false>(a);
 }
 
+// Key-range pieces always run as split 128-query workgroups: the grids that need pieces are
+// the ones too small for anything else.
+template <typename TR>
+hipError_t launch_fwd_part_dt(const FwdArgs& a) {
+  if (a.D == 64)
+    return a.causal ? launch_fwd_nw<TR, 64, true, 8, 2, true>(a) : launch_fwd_nw<TR, 64, false, 8, 2, true>(a);
+  return a.causal ? launch_fwd_nw<TR, 128, true, 8, 2, true>(a) : launch_fwd_nw<TR, 128, false, 8, 2, true>(a);
+}
+
+// ---------------------------------------------------------------- merge of partials
+// Attention over a union of disjoint key sets from the results over each set: with m the
+// largest partial LSE, w_s = exp(LSE_s - m), LSE = m + log(sum_s w_s) and
+// O = sum_s (w_s / sum_s w_s) O_s.  A part with LSE_s = -inf (no key) has weight 0.  One
+// thread handles 8 columns of one row; parts are summed in index order (deterministic).
+template <typename TR, int HD>
+__global__ void __launch_bounds__(256)
+merge_kernel(const float* __restrict__ Op, const float* __restrict__ Lp, int n_part, long long rows,
+             uint16_t* __restrict__ O, float* __restrict__ LSE) {
+  constexpr int TPR = HD / 8;
+  const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int d0 = (threadIdx.x % TPR) * 8;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < n_part; ++s) m = fmaxf(m, Lp[s * rows + row]);
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+  float wsum = 0.f;
+  if (m > -INFINITY) {
+    for (int s = 0; s < n_part; ++s) {
+      const float w = __expf(Lp[s * rows + row] - m);
+      const float* src = Op + ((size_t)s * rows + row) * HD + d0;
+      o0 += w * *reinterpret_cast<const f32x4*>(src);
+      o1 += w * *reinterpret_cast<const f32x4*>(src + 4);
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *reinterpret_cast<u32x4*>(O + row * HD + d0) =
+      u32x4{TR::pack(o0[0] * inv, o0[1] * inv), TR::pack(o0[2] * inv, o0[3] * inv),
+            TR::pack(o1[0] * inv, o1[1] * inv), TR::pack(o1[2] * inv, o1[3] * inv)};
+  if (d0 == 0) LSE[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
+template <typename TR, int HD>
+hipError_t launch_merge_t(const MergeArgs& a) {
+  constexpr int RPB = 256 / (HD / 8);
+  hipLaunchKernelGGL((merge_kernel<TR, HD>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(256), 0, a.stream,
+                     a.o_part, a.lse_part, a.n_part, a.rows, static_cast<uint16_t*>(a.o), a.lse);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.n_part > 1) return a.bf16 ? launch_fwd_part_dt<Bf16>(a) : launch_fwd_part_dt<F16>(a);
   return a.bf16 ? launch_fwd_dt<Bf16>(a) : launch_fwd_dt<F16>(a);
+}
+
+hipError_t launch_merge(const MergeArgs& a) {
+  if (a.bf16) return a.D == 64 ? launch_merge_t<Bf16, 64>(a) : launch_merge_t<Bf16, 128>(a);
+  return a.D == 64 ? launch_merge_t<F16, 64>(a) : launch_merge_t<F16, 128>(a);
+}
+
+// Pieces of the key range for fa_fwd_splitkv when the caller leaves the choice to the library:
+// grids that already fill the CUs take none (1); smaller ones take enough pieces for one split
+// 128-query workgroup per CU (measured: more pieces cost more in partial traffic and merging
+// than they gain), while every half-piece keeps at least four 64-key tiles.
+int fwd_auto_parts(long long B, long long Hq, long long N, long long D, bool causal) {
+  (void)D;
+  if (B * Hq * ((N + 255) / 256) >= 512) return 1;
+  const long long tiles = B * Hq * ((N + 127) / 128);
+  const long long T = (N + 63) / 64 / (causal ? 2 : 1);
+  long long parts = (256 + tiles - 1) / tiles;
+  parts = parts < T / 8 ? parts : T / 8;
+  return (int)(parts < 1 ? 1 : (parts > 64 ? 64 : parts));
 }
 
 }  // namespace fa

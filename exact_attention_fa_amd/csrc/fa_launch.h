@@ -19,6 +19,21 @@ struct FwdArgs {
   bool causal;
   bool bf16;
   hipStream_t stream;
+  int n_part = 1;            // > 1: key-range pieces written as fp32 partials (o_part, lse_part)
+  float* o_part = nullptr;   // (n_part, B, Hq, N, D)
+  float* lse_part = nullptr; // (n_part, B, Hq, N)
+};
+
+// Merge of fp32 partial results over disjoint key sets (see fa_merge_partials).
+struct MergeArgs {
+  const float* o_part;   // (n_part, rows, D)
+  const float* lse_part; // (n_part, rows)
+  int n_part;
+  long long rows, D;
+  void* o;
+  float* lse;
+  bool bf16;
+  hipStream_t stream;
 };
 
 // Workspace carve-up used by the backward stages (byte offsets from the base).
@@ -50,6 +65,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_merge(const MergeArgs& a);
+int fwd_auto_parts(long long B, long long Hq, long long N, long long D, bool causal);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);

@@ -71,7 +71,8 @@ enum fa_status {
   FA_ERR_WORKSPACE = 8,    /* workspace_bytes < fa_bwd_workspace_size(...) */
   FA_ERR_HIP = 9,          /* the HIP runtime rejected a launch */
   FA_ERR_TOO_LARGE = 10,   /* a size exceeds the 32-bit index range the kernels use */
-  FA_ERR_ALIAS = 11        /* an output buffer overlaps another buffer of the call */
+  FA_ERR_ALIAS = 11,       /* an output buffer overlaps another buffer of the call */
+  FA_ERR_SPLIT = 12        /* a split / part count is out of range */
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -88,6 +89,42 @@ const char* fa_status_string(int status);
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
            float softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * Forward with the key range of every query tile cut into n_split contiguous pieces, for
+ * grids too small to fill the GPU (few batch x head x query tiles, long sequences: the
+ * per-GPU share of a head-sharded problem).  Each piece writes its normalised output and
+ * log-sum-exp as fp32 partials into the workspace, and a merge pass (fa_merge_partials)
+ * combines them through the LSEs ("FlashNystrom", section "Latency": splitting the work of
+ * one output over several workgroups keeps a low batch x head grid busy).  Same inputs,
+ * outputs and conventions as fa_fwd; the result equals fa_fwd's up to the rounding order
+ * and is bitwise deterministic for a given n_split.
+ *   n_split    1..64 pieces, or 0 for fa_fwd_splitkv_parts(...) (the library's choice).
+ *              A resolved count of 1 is exactly fa_fwd, and the workspace may then be NULL.
+ *   workspace  caller-owned device memory of at least
+ *              fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, n) bytes for the resolved n:
+ *              n x (B, Hq, N, D) fp32 outputs and n x (B, Hq, N) fp32 LSEs, 256-byte aligned.
+ * Errors as fa_fwd, plus FA_ERR_SPLIT (n_split outside 0..64) and FA_ERR_WORKSPACE.
+ */
+int fa_fwd_splitkv_parts(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int causal);
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int n_split);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, int n_split, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                   int64_t D, float softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * Merge of attention results over disjoint key sets (the merge step of fa_fwd_splitkv, and
+ * the step a sequence-parallel port would use to combine per-block results).  For each of
+ * `rows` rows, part s holds the output over its key set, normalised, o_parts[(s*rows + r)*D + d]
+ * (fp32), and its natural-log log-sum-exp lse_parts[s*rows + r] (-inf for an empty set).
+ * With m = max_s LSE_s and w_s = exp(LSE_s - m):
+ *   lse[r] = m + log(sum_s w_s),   o[r] = sum_s (w_s / sum_s w_s) o_s[r]   (rounded to dtype)
+ * A row whose parts are all empty gets o = 0 and lse = -inf.  Parts are summed in index order
+ * (deterministic).  n_parts 1..64; D 64 or 128; o and o_parts 16-byte aligned, lse and
+ * lse_parts 4-byte aligned.
+ */
+int fa_merge_partials(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
+                      int64_t rows, int64_t D, int dtype, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs: the fp32 D = rowsum(dO * O) and LSE * log2(e)

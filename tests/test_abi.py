@@ -15,6 +15,7 @@ STATUS = {
     "FA_OK": 0, "FA_ERR_NULL_POINTER": 1, "FA_ERR_BAD_SHAPE": 2, "FA_ERR_HEAD_DIM": 3,
     "FA_ERR_GQA": 4, "FA_ERR_DTYPE": 5, "FA_ERR_SCALE": 6, "FA_ERR_ALIGNMENT": 7,
     "FA_ERR_WORKSPACE": 8, "FA_ERR_HIP": 9, "FA_ERR_TOO_LARGE": 10, "FA_ERR_ALIAS": 11,
+    "FA_ERR_SPLIT": 12,
 }
 
 # Fake, aligned, non-null "device" addresses: every call below fails validation before any
@@ -60,8 +61,8 @@ def test_header_status_values_match():
 
 
 def test_version_and_strings(lib):
-    assert fa.fa_version() == 10000
-    for code in range(12):
+    assert fa.fa_version() == 10100
+    for code in range(13):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status"
     assert fa.fa_status_string(999) == "unknown status"
@@ -157,6 +158,62 @@ def test_stage_entry_points_reject(lib):
         STATUS["FA_ERR_NULL_POINTER"]
     assert lib.fa_bwd_postprocess(ptr(1), ptr(2), ptr(1), need, B, Hq, Hkv, N, D, 1, None) == \
         STATUS["FA_ERR_ALIAS"]
+
+
+def test_splitkv_workspace_and_parts(lib):
+    B, Hq, Hkv, N, D = 1, 2, 1, 3000, 128
+    up = lambda x: (x + 255) // 256 * 256
+    rows = B * Hq * N
+    assert fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, 3) == up(3 * rows * D * 4) + up(3 * rows * 4)
+    assert fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, 1) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, 0) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, 65) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, 80, 2) == 0
+    # grids that fill the GPU take no pieces; one head of a long sequence takes several
+    assert fa.fa_fwd_splitkv_parts(4, 16, 16, 4096, 128, False) == 1
+    assert fa.fa_fwd_splitkv_parts(1, 1, 1, 16384, 128, False) == 2
+    assert fa.fa_fwd_splitkv_parts(1, 1, 1, 8192, 64, True) == 4
+    assert fa.fa_fwd_splitkv_parts(1, 16, 4, 2048, 64, True) == 1
+    assert fa.fa_fwd_splitkv_parts(1, 1, 1, 100, 64, False) == 1
+    assert fa.fa_fwd_splitkv_parts(1, 1, 1, 100, 96, False) == 0
+
+
+def splitkv(lib, n_split=2, ws_bytes=None, B=1, Hq=2, Hkv=2, N=4096, D=128, scale=0.1, dtype=1, **over):
+    names = ["q", "k", "v", "o", "lse", "ws"]
+    ptrs = {n: ptr(i) for i, n in enumerate(names)}
+    ptrs.update({n: x if isinstance(x, ctypes.c_void_p) else ptr(x) for n, x in over.items()})
+    if ws_bytes is None:
+        ws_bytes = fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, max(n_split, 1))
+    return lib.fa_fwd_splitkv(*[ptrs[n] for n in names[:5]], ptrs["ws"], ws_bytes, n_split, B, Hq, Hkv, N, D,
+                              scale, 0, dtype, None)
+
+
+def test_splitkv_rejects(lib):
+    assert splitkv(lib, n_split=-1) == STATUS["FA_ERR_SPLIT"]
+    assert splitkv(lib, n_split=65) == STATUS["FA_ERR_SPLIT"]
+    assert splitkv(lib, n_split=3, ws_bytes=fa.fa_fwd_splitkv_workspace_size(1, 2, 2, 4096, 128, 3) - 1) == \
+        STATUS["FA_ERR_WORKSPACE"]
+    assert splitkv(lib, ws=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]
+    assert splitkv(lib, ws=ctypes.c_void_p(A + 64)) == STATUS["FA_ERR_ALIGNMENT"]
+    assert splitkv(lib, ws=ptr(3)) == STATUS["FA_ERR_ALIAS"]
+    assert splitkv(lib, D=96) == STATUS["FA_ERR_HEAD_DIM"]
+    assert splitkv(lib, scale=float("nan")) == STATUS["FA_ERR_SCALE"]
+    # a resolved count of 1 is fa_fwd's own validation (no workspace needed)
+    assert splitkv(lib, n_split=1, ws=ctypes.c_void_p(0), o=0) == STATUS["FA_ERR_ALIAS"]
+
+
+def test_merge_rejects(lib):
+    def merge(op=0, lp=1, n=2, o=2, l=3, rows=100, D=128, dtype=1):
+        P = lambda x: x if isinstance(x, ctypes.c_void_p) else ptr(x)
+        return lib.fa_merge_partials(P(op), P(lp), n, P(o), P(l), rows, D, dtype, None)
+    assert merge(n=0) == STATUS["FA_ERR_SPLIT"]
+    assert merge(n=65) == STATUS["FA_ERR_SPLIT"]
+    assert merge(rows=0) == STATUS["FA_ERR_BAD_SHAPE"]
+    assert merge(D=32) == STATUS["FA_ERR_HEAD_DIM"]
+    assert merge(dtype=3) == STATUS["FA_ERR_DTYPE"]
+    assert merge(op=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]
+    assert merge(op=ctypes.c_void_p(A + 4)) == STATUS["FA_ERR_ALIGNMENT"]
+    assert merge(o=0) == STATUS["FA_ERR_ALIAS"]
 
 
 def test_python_binding_refuses_cpu_tensors():
