@@ -71,16 +71,23 @@ int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long long N, long long D) {
   BwdWorkspace w{};
   const size_t rows = (size_t)B * (size_t)Hq * (size_t)N;
+  w.n_qp = bwd_query_pieces(B, Hq, N);
+  w.n_kp = bwd_key_pieces(B, Hq, N, D);
+  w.partial_dkdv = Hq != Hkv || w.n_qp > 1;
   size_t off = 0;
   w.delta = off;
   off += round_up(rows * 4);
   w.lse2 = off;
   off += round_up(rows * 4);
-  if (Hq != Hkv) {
+  if (w.partial_dkdv) {
     w.dk_part = off;
-    off += round_up(rows * (size_t)D * 4);
+    off += round_up(rows * (size_t)w.n_qp * (size_t)D * 4);
     w.dv_part = off;
-    off += round_up(rows * (size_t)D * 4);
+    off += round_up(rows * (size_t)w.n_qp * (size_t)D * 4);
+  }
+  if (w.n_kp > 1) {
+    w.dq_part = off;
+    off += round_up(rows * (size_t)w.n_kp * (size_t)D * 4);
   }
   w.total = off;
   return w;
@@ -264,7 +271,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, v
   FA_TRY(check_scale(softmax_scale));
   const void* p16[] = {q, k, v, dout};
   for (const void* p : p16) FA_TRY(check_ptr(p, 16));
-  const bool direct = Hq == Hkv;
+  const bool direct = !bwd_workspace_layout(B, Hq, Hkv, N, D).partial_dkdv;
   if (direct) {
     FA_TRY(check_ptr(dk, 16));
     FA_TRY(check_ptr(dv, 16));
@@ -287,8 +294,9 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
   const void* p16[] = {q, k, v, dout, dq};
   for (const void* p : p16) FA_TRY(check_ptr(p, 16));
   const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const BwdWorkspace w = bwd_workspace_layout(B, Hq, Hkv, N, D);
   const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {dout, qb, false}, {dq, qb, true},
-                     {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, false}};
+                     {workspace, w.total, w.n_kp > 1}};
   FA_TRY(check_alias(r, 6));
   const BwdArgs a = make_bwd_args(q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, D,
                                   softmax_scale, causal, dtype, stream);

@@ -32,6 +32,12 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
+
+#define FA_HIP_TRY(expr)                       \
+  do {                                         \
+    const hipError_t _e = (expr);              \
+    if (_e != hipSuccess) return _e;           \
+  } while (0)
 constexpr int kBwdBKV = 128;  // keys per workgroup (32 per wave)
 constexpr int kBwdBQ = 64;    // query rows per streamed tile
 constexpr int kDqBC = 32;     // dQ kernel: keys per K/V tile
@@ -81,7 +87,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
                 uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int Hq, int Hkv,
-                int N, int n_kt, float c2, float scale, int snake) {
+                int N, int n_kt, float c2, float scale, int snake, int n_qp) {
   constexpr int BKV = kBwdBKV, BQ = kBwdBQ;
   constexpr int KST = HD / 16, DB = HD / 32;
   constexpr int QT_BYTES = BQ * HD * 2;
@@ -100,7 +106,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
 
-  const int job = xcd_remap(blockIdx.x, gridDim.x);
+  int job = xcd_remap(blockIdx.x, gridDim.x);
+  // Small grids cut the query range of each key block into n_qp pieces, one workgroup each,
+  // whose partials the postprocess sums (PARTIAL).
+  const int piece = job % n_qp;
+  job /= n_qp;
   // causal: low kt has the most query tiles
   const int kt = CAUSAL ? n_kt - 1 - causal_tile(job % n_kt, job / n_kt, n_kt, snake) : job % n_kt;
   const int bh = job / n_kt;
@@ -115,8 +125,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int kv0 = kt * BKV;
   const int kw0 = kv0 + wave * 32;  // this wave's first key
   const int key = kw0 + c;          // the key this lane's accumulator column belongs to
-  const int n_qt = (N + BQ - 1) / BQ;
+  const int n_qt_all = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kv0 / BQ : 0;  // earlier query tiles see none of these keys
+  // this workgroup's query tiles [q_lo, n_qt): piece `piece` of [qt0, n_qt_all)
+  const int q_lo = qt0 + (int)((long long)(n_qt_all - qt0) * piece / n_qp);
+  const int n_qt = qt0 + (int)((long long)(n_qt_all - qt0) * (piece + 1) / n_qp);
 
   // Direct loads of one 64-query tile of Q, dO, L2 and D into buffer slot `sl`.
   const uint32_t rowb = (uint32_t)N * HD * 2u;
@@ -140,8 +153,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (wave == 0) dma_to_lds<4>(rL, (uint32_t)lane * 4u, q0 * 4u, dst + OFF_L);
     if (wave == 1) dma_to_lds<4>(rD, (uint32_t)lane * 4u, q0 * 4u, dst + OFF_D);
   };
-  if (qt0 < n_qt) issue(qt0, smem);
-  if (qt0 + 1 < n_qt) issue(qt0 + 1, smem + SLOT);
+  if (q_lo < n_qt) issue(q_lo, smem);
+  if (q_lo + 1 < n_qt) issue(q_lo + 1, smem + SLOT);
 
   // K and V rows of this lane's key as B operands: slot j of k-step kk = K[key][kk*16 + g*8 + j]
   // (zero past the end: those keys' dK/dV are never stored).
@@ -310,7 +323,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       unit(masked_tag, std::true_type{}, qt, 1, cur, nxt, s1, dp1, s0, dp0);
   };
 
-  if (qt0 < n_qt) {
+  if (q_lo < n_qt) {
     // prologue: S/dP of the first unit
     wait_vmcnt<0>();
     lds_barrier();
@@ -329,8 +342,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
     // causal: the first two tiles hold this workgroup's diagonal; every later tile is
     // entirely below it
-    const int qt_m = CAUSAL ? min(n_qt, qt0 + 2) : qt0;
-    int qt = qt0;
+    const int qt_m = CAUSAL ? min(n_qt, qt0 + 2) : q_lo;
+    int qt = q_lo;
     for (; qt < qt_m && qt < n_qt - 1; ++qt) run(std::true_type{}, std::false_type{}, qt);
     for (; qt < n_qt - 1; ++qt) run(std::false_type{}, std::false_type{}, qt);
     if (qt < qt_m)
@@ -348,7 +361,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       if (kr_ >= N) continue;
       const int d = db * 32 + c;
       if (PARTIAL) {
-        const size_t off = ((size_t)bh * N + kr_) * HD + d;
+        const size_t off = (((size_t)bh * n_qp + piece) * N + kr_) * HD + d;
         dKp[off] = dKa[db][i] * scale;
         dVp[off] = dVa[db][i];
       } else {
@@ -374,12 +387,15 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // SPLIT = 2: two wave groups own the same query rows and take the two halves of the key range,
 // each with its own LDS buffers; group 1 hands its dQ^T partial to group 0 through LDS at the
 // end (one fixed-order addition, still deterministic).
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
+// PART: small grids also cut each query tile's key range into n_kp pieces, one workgroup
+// each; a piece writes its unscaled fp32 dQ partial (dQp) and bwd_dq_sum_kernel adds them.
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
-              int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake) {
+              int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake, int n_kp,
+              float* __restrict__ dQp) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
   constexpr int GW = NW / SPLIT;            // waves per group
   constexpr int BR = GW * 32, BC = kDqBC;  // query rows per workgroup (32 per wave), keys per tile
@@ -400,7 +416,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wv = wave % GW;   // wave within the group
   const int c = lane & 31, g = lane >> 5;
 
-  const int job = xcd_remap(blockIdx.x, gridDim.x);
+  int job = xcd_remap(blockIdx.x, gridDim.x);
+  int part = 0;  // piece of the key range (PART)
+  if constexpr (PART) {
+    part = job % n_kp;
+    job /= n_kp;
+  }
   int qt = job % n_qt;
   const int bh = job / n_qt;
   if (CAUSAL) qt = causal_tile(qt, bh, n_qt, snake);
@@ -422,9 +443,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // This group's tiles [t0, t0 + Tg) (group 0 takes the larger half), the steps every wave
   // takes (the larger group's tile count), and how many of the group's tiles this wave
   // computes on; the wave's diagonal tile Tw - 1, when in the group's range, is its last.
-  const int half = SPLIT == 2 ? (T + 1) / 2 : T;
-  const int t0 = grp ? half : 0;
-  const int Tg = grp ? T - half : half;
+  const int tb = PART ? (int)((long long)T * part / n_kp) : 0;  // this workgroup's piece [tb, te)
+  const int te = PART ? (int)((long long)T * (part + 1) / n_kp) : T;
+  const int half = SPLIT == 2 ? (te - tb + 1) / 2 : te - tb;
+  const int t0 = tb + (grp ? half : 0);
+  const int Tg = grp ? te - tb - half : half;
   const int Twg = max(0, min(Tw - t0, Tg));
 
   // Direct loads of K/V tile t (keys past the end read as zero).
@@ -645,6 +668,18 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 
   // ---- epilogue: register i of acc[db] <-> dQ[qi][db*32 + (i/4)*8 + g*4 + i%4]
+  if constexpr (PART) {
+    if (qi < N) {
+      float* const prow = dQp + (((size_t)bh * n_kp + part) * N + qi) * HD;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4*>(prow + db * 32 + i4 * 8 + g * 4) =
+              f32x4{acc[db][i4 * 4 + 0], acc[db][i4 * 4 + 1], acc[db][i4 * 4 + 2], acc[db][i4 * 4 + 3]};
+    }
+    return;
+  }
   if (qi < N) {
     uint16_t* const qrow = dQ + (size_t)bh * N * HD + (size_t)qi * HD;
 #pragma unroll
@@ -684,6 +719,27 @@ bwd_post_dkdv_kernel(const float* __restrict__ dKp, const float* __restrict__ dV
       u32x4{TR::pack(va[0], va[1]), TR::pack(va[2], va[3]), TR::pack(vb[0], vb[1]), TR::pack(vb[2], vb[3])};
 }
 
+// dQ of row (bh, n) = scale * the sum, in piece order, of its n_kp fp32 partials.
+template <typename TR, int HD>
+__global__ void __launch_bounds__(kThreads)
+bwd_dq_sum_kernel(const float* __restrict__ dQp, uint16_t* __restrict__ dQ, int n_kp, int N, float scale,
+                  long long n8) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n8) return;
+  constexpr int C8 = HD / 8;
+  const long long row = i / C8, bh = row / N, n = row % N;
+  const int d0 = (int)(i % C8) * 8;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = a;
+  for (int p = 0; p < n_kp; ++p) {
+    const float* src = dQp + ((bh * n_kp + p) * N + n) * HD + d0;
+    a += *reinterpret_cast<const f32x4*>(src);
+    c += *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  *reinterpret_cast<u32x4*>(dQ + i * 8) =
+      u32x4{TR::pack(a[0] * scale, a[1] * scale), TR::pack(a[2] * scale, a[3] * scale),
+            TR::pack(c[0] * scale, c[1] * scale), TR::pack(c[2] * scale, c[3] * scale)};
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <typename TR, int HD>
@@ -706,7 +762,7 @@ template <typename TR, int HD, bool CAUSAL, bool PARTIAL>
 hipError_t dkdv_t(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
   const int n_kt = (int)((a.N + kBwdBKV - 1) / kBwdBKV);
-  const long long blocks = a.B * a.Hq * (long long)n_kt;
+  const long long blocks = a.B * a.Hq * (long long)n_kt * w.n_qp;
   float* const dkp = PARTIAL ? reinterpret_cast<float*>(a.ws + w.dk_part) : nullptr;
   float* const dvp = PARTIAL ? reinterpret_cast<float*>(a.ws + w.dv_part) : nullptr;
   hipLaunchKernelGGL((bwd_dkdv_kernel<TR, HD, CAUSAL, PARTIAL>), dim3((unsigned)blocks), dim3(kThreads), 0,
@@ -714,29 +770,37 @@ hipError_t dkdv_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dkp, dvp, (int)a.Hq, (int)a.Hkv,
-                     (int)a.N, n_kt, exp2_factor(a.scale), a.scale, (int)grid_fits(blocks, 1));
+                     (int)a.N, n_kt, exp2_factor(a.scale), a.scale, (int)grid_fits(blocks, 1), w.n_qp);
   return hipGetLastError();
 }
 
 template <typename TR, int HD>
 hipError_t dkdv_hd(const BwdArgs& a) {
-  const bool partial = a.Hq != a.Hkv;
+  const bool partial = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D).partial_dkdv;
   if (a.causal) return partial ? dkdv_t<TR, HD, true, true>(a) : dkdv_t<TR, HD, true, false>(a);
   return partial ? dkdv_t<TR, HD, false, true>(a) : dkdv_t<TR, HD, false, false>(a);
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false>
 hipError_t dq_nw(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
   constexpr int BR = NW / SPLIT * 32;
   const int n_qt = (int)((a.N + BR - 1) / BR);
-  const long long blocks = a.B * a.Hq * (long long)n_qt;
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
+  const int n_kp = PART ? w.n_kp : 1;
+  const long long blocks = a.B * a.Hq * (long long)n_qt * n_kp;
+  float* const dqp = PART ? reinterpret_cast<float*>(a.ws + w.dq_part) : nullptr;
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT, PART>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dq), (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, exp2_factor(a.scale),
-                     a.scale, (int)grid_fits(blocks, 8 / NW));
+                     a.scale, (int)grid_fits(blocks, 8 / NW), n_kp, dqp);
+  if constexpr (PART) {
+    FA_HIP_TRY(hipGetLastError());
+    const long long n8 = a.B * a.Hq * a.N * a.D / 8;
+    hipLaunchKernelGGL((bwd_dq_sum_kernel<TR, HD>), dim3((unsigned)((n8 + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, a.stream, dqp, static_cast<uint16_t*>(a.dq), n_kp, (int)a.N, a.scale, n8);
+  }
   return hipGetLastError();
 }
 
@@ -750,6 +814,7 @@ hipError_t dq_t(const BwdArgs& a) {
   const long long big = a.B * a.Hq * ((a.N + 255) / 256);
   if constexpr (HD == 128)
     if (big >= 512) return dq_nw<TR, HD, CAUSAL, 8, 1>(a);
+  if (bwd_key_pieces(a.B, a.Hq, a.N, a.D) > 1) return dq_nw<TR, HD, CAUSAL, 8, 2, true>(a);
   if (a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512) return dq_nw<TR, HD, CAUSAL, 8, 2>(a);
   return dq_nw<TR, HD, CAUSAL, 4, 1>(a);
 }
@@ -762,17 +827,40 @@ hipError_t dq_dt(const BwdArgs& a) {
 
 template <typename TR>
 hipError_t post_t(const BwdArgs& a) {
-  if (a.Hq == a.Hkv) return hipSuccess;  // dK and dV were written directly
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
+  if (!w.partial_dkdv) return hipSuccess;  // dK and dV were written directly
   const long long kv8 = a.B * a.Hkv * a.N * a.D / 8;
   hipLaunchKernelGGL((bwd_post_dkdv_kernel<TR>), dim3((unsigned)((kv8 + kThreads - 1) / kThreads)), dim3(kThreads),
                      0, a.stream, reinterpret_cast<const float*>(a.ws + w.dk_part),
                      reinterpret_cast<const float*>(a.ws + w.dv_part), static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), (int)(a.Hq / a.Hkv), a.N * a.D / 8, kv8);
+                     static_cast<uint16_t*>(a.dv), (int)(a.Hq / a.Hkv) * w.n_qp, a.N * a.D / 8, kv8);
   return hipGetLastError();
 }
 
 }  // namespace
+
+// Query-range pieces of the dK/dV pass (one 4-wave workgroup per CU): enough for every CU to
+// get one workgroup, each piece keeping at least eight 64-query tiles.
+int bwd_query_pieces(long long B, long long Hq, long long N) {
+  const long long grid = B * Hq * ((N + kBwdBKV - 1) / kBwdBKV);
+  if (grid >= 256) return 1;
+  long long p = (256 + grid - 1) / grid;
+  const long long cap = (N + kBwdBQ - 1) / kBwdBQ / 8;
+  p = p < cap ? p : cap;
+  return (int)(p < 1 ? 1 : (p > 64 ? 64 : p));
+}
+
+// Key-range pieces of the dQ pass where it runs as split 128-query workgroups (one per CU),
+// each half-piece keeping at least four 32-key tiles.
+int bwd_key_pieces(long long B, long long Hq, long long N, long long D) {
+  if (D == 128 && B * Hq * ((N + 255) / 256) >= 512) return 1;
+  const long long grid = B * Hq * ((N + 127) / 128);
+  if (grid >= 256) return 1;
+  long long p = (256 + grid - 1) / grid;
+  const long long cap = (N + kDqBC - 1) / kDqBC / 8;
+  p = p < cap ? p : cap;
+  return (int)(p < 1 ? 1 : (p > 64 ? 64 : p));
+}
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a) {
   if (a.bf16) return a.D == 64 ? pre_t<Bf16, 64>(a) : pre_t<Bf16, 128>(a);

@@ -40,10 +40,17 @@ struct MergeArgs {
 struct BwdWorkspace {
   size_t delta;    // fp32 (B, Hq, N): D = rowsum(dO * O)
   size_t lse2;     // fp32 (B, Hq, N): LSE * log2(e)
-  size_t dk_part;  // fp32 (B, Hq, N, D): per-query-head dK partials (only when Hq > Hkv)
-  size_t dv_part;  // fp32 (B, Hq, N, D): per-query-head dV partials (only when Hq > Hkv)
+  size_t dk_part;  // fp32 (B, Hq, n_qp, N, D): dK partials per query head and query-range piece
+  size_t dv_part;  // fp32 (B, Hq, n_qp, N, D): dV partials (both only when partial_dkdv)
+  size_t dq_part;  // fp32 (B, Hq, n_kp, N, D): dQ partials per key-range piece (only when n_kp > 1)
+  int n_qp;        // query-range pieces of the dK/dV pass
+  int n_kp;        // key-range pieces of the dQ pass
+  bool partial_dkdv;  // the dK/dV pass writes partials (Hq > Hkv or n_qp > 1)
   size_t total;
 };
+// Pieces for grids too small to occupy every CU (depend on the shape only).
+int bwd_query_pieces(long long B, long long Hq, long long N);
+int bwd_key_pieces(long long B, long long Hq, long long N, long long D);
 BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long long N, long long D);
 
 struct BwdArgs {

@@ -108,6 +108,10 @@ def test_workspace_size(lib):
     assert fa.fa_bwd_workspace_size(B, Hq, Hq, N, D) == mha
     assert fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D) == mha + 2 * up(rows * D * 4)
     assert fa.fa_bwd_workspace_size(0, Hq, Hkv, N, D) == 0
+    # one head of a long sequence: the dK/dV pass takes 2 query-range pieces and the dQ pass
+    # 2 key-range pieces, each with fp32 partials
+    r1 = 16384
+    assert fa.fa_bwd_workspace_size(1, 1, 1, r1, D) == 2 * up(r1 * 4) + 2 * up(2 * r1 * D * 4) + up(2 * r1 * D * 4)
     assert fa.fa_bwd_workspace_size(B, Hq, Hkv, N, 96) == 0
 
 

@@ -74,9 +74,13 @@ LARGE_GRID = [
     (2, 64, 16, 1030, 128, "fp16", True),
     (2, 32, 8, 1000, 64, "fp16", False),
     (1, 64, 64, 900, 128, "bf16", False),
-    # split key range over many tiles per group, GQA, ragged
+    # split key range over many tiles per group, GQA, ragged; these grids are also small
+    # enough for the backward to cut query and key ranges into pieces (2-3 here)
     (1, 8, 2, 2000, 128, "bf16", False),
     (1, 8, 8, 1500, 64, "fp16", True),
+    # tiny grids: many backward pieces (dK/dV 5 and dQ 11; dK/dV 4 and dQ 4)
+    (1, 1, 1, 3000, 128, "bf16", True),
+    (1, 2, 1, 4100, 64, "fp16", False),
 ]
 
 

@@ -1,5 +1,7 @@
-"""GPU parity of the split-key-range forward (fa_fwd_splitkv) and of the merge of partial
-results (fa_merge_partials), against the CPU oracle, through the C ABI.
+"""GPU parity of the small-grid paths against the CPU oracle, through the C ABI: the
+split-key-range forward (fa_fwd_splitkv), the merge of partial results (fa_merge_partials),
+and the backward's query- and key-range pieces on the per-GPU share of a head-sharded
+long-context problem.
 
 The merge is checked on partials the oracle computes itself (attention over disjoint slices
 of the keys, plus an empty part), so it is pinned to the oracle's full result independently
@@ -78,6 +80,19 @@ def test_splitkv_auto_on_one_head_long_sequence():
     rows = np.unique(np.concatenate([[0, 63, 64, 8191, 16383], rng.choice(16384, 60, replace=False)]))
     o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v), shape.scale, True, rows=rows)
     log("  n", n, "errors", assert_fwd_close(f64(o)[:, :, rows], f64(lse)[:, :, rows], o_ref, lse_ref, str(shape)))
+
+
+def test_backward_pieces_on_one_head_long_sequence():
+    """One head, N = 16384, causal: the backward cuts the dK/dV pass's query ranges and the dQ
+    pass's key ranges into pieces; sampled rows and keys match the oracle."""
+    import exact_attention_fa_amd as fa
+    from parity_util import sampled_check
+    shape = Shape(1, 1, 1, 16384, 128, "bf16", True, 0.5)
+    ws = fa.fa_bwd_workspace_size(1, 1, 1, 16384, 128)
+    rows = 16384
+    assert ws > 2 * rows * 4 + 3 * rows * 128 * 4, "expected partial buffers for the pieces"
+    errs, _ = sampled_check(shape, 4343, units=[(0, 0)], n_rows=48, backward=True)
+    log("  errors", errs)
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64)])
