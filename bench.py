@@ -2,7 +2,9 @@
 """Benchmark of the fused exact-attention hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input: the forward
-(fa_fwd) and the backward (preprocess, dK/dV pass, dQ pass, postprocess) on the same stream.
+(fa_fwd_splitkv with the library's choice of key-range pieces, which is exactly fa_fwd
+except on grids too small to fill the GPU) and the backward (preprocess, dK/dV pass, dQ
+pass, postprocess) on the same stream.
 Inputs, outputs and workspace are allocated and resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout:
@@ -43,6 +45,7 @@ WORKLOAD_KEYS = {
     "fwd_bf16_n8192": ("fwd_bf16_long", 0),
     "fwd_bf16_n16384": ("fwd_bf16_long", 1),
     "causal_long_bf16": ("causal_long_bf16", 0),
+    "shard_causal_bf16_h1": ("shard_causal_bf16", 0),
 }
 for _i, (_n, _d) in enumerate([(2048, 64), (2048, 128), (4096, 64), (4096, 128), (4000, 64), (4000, 128)]):
     WORKLOAD_KEYS[f"gqa_causal_fp16_n{_n}_d{_d}"] = ("gqa_causal_fp16", _i)
@@ -178,6 +181,10 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D), dtype=torch.uint8, device=dev)
     causal, scale = shape.causal, shape.scale
+    # the forward takes key-range pieces only where the grid is too small to fill the GPU
+    n_split = fa.fa_fwd_splitkv_parts(B, Hq, Hkv, N, D, causal)
+    fws = torch.empty(max(fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, n_split), 256), dtype=torch.uint8,
+                      device=dev)
     stream = torch.cuda.current_stream(dev)
 
     kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_postprocess"]
@@ -185,7 +192,8 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fa_fwd(q, k, v, causal=causal, softmax_scale=scale, out=o, lse=lse)
+        fa.fa_fwd_splitkv(q, k, v, causal=causal, softmax_scale=scale, n_split=n_split, workspace=fws, out=o,
+                          lse=lse)
         if ev is not None:
             ev[1].record(stream)
         fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
@@ -257,7 +265,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D,
                    "causal": causal, "softmax_scale": scale, "inputs": "N(0,1) seeded, cast RNE"
-                   + (f", x{shape.mult}" if shape.mult != 1.0 else "")},
+                   + (f", x{shape.mult}" if shape.mult != 1.0 else ""), "fwd_key_pieces": n_split},
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
         "fwd_pct_peak": round(100 * f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 2),

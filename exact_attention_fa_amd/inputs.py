@@ -63,6 +63,8 @@ WORKLOADS = {
     "gqa_causal_fp16": [Shape(1, 16, 4, n, d, "fp16", True)
                         for n in (2048, 4096, 4000) for d in (64, 128)],
     "causal_long_bf16": [Shape(1, 8, 8, 16384, 128, "bf16", True, 0.5)],
+    # one GPU's share of the long causal workload sharded by heads over 8 GPUs
+    "shard_causal_bf16": [Shape(1, 1, 1, 16384, 128, "bf16", True, 0.5)],
 }
 WORKLOAD_IDS = {name: i + 1 for i, name in enumerate(WORKLOADS)}
 
