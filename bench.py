@@ -51,13 +51,15 @@ for _i, (_n, _d) in enumerate([(2048, 64), (2048, 128), (4096, 64), (4096, 128),
     WORKLOAD_KEYS[f"gqa_causal_fp16_n{_n}_d{_d}"] = ("gqa_causal_fp16", _i)
 
 
-# Which sources each timed kernel is built from (for matching a counter summary to the code).
+# Which sources (and build options) each timed kernel is built from, for matching a counter
+# summary to the code.
+_DEV = ["exact_attention_fa_amd/csrc/fa_device.h", "exact_attention_fa_amd/_build.py"]
 KERNEL_SOURCES = {
-    "fwd": ["exact_attention_fa_amd/csrc/fa_fwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
-    "bwd_preprocess": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
-    "bwd_dkdv": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
-    "bwd_dq": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
-    "bwd_postprocess": ["exact_attention_fa_amd/csrc/fa_bwd.hip", "exact_attention_fa_amd/csrc/fa_device.h"],
+    "fwd": ["exact_attention_fa_amd/csrc/fa_fwd.hip", *_DEV],
+    "bwd_preprocess": ["exact_attention_fa_amd/csrc/fa_bwd.hip", *_DEV],
+    "bwd_dkdv": ["exact_attention_fa_amd/csrc/fa_bwd.hip", *_DEV],
+    "bwd_dq": ["exact_attention_fa_amd/csrc/fa_bwd.hip", *_DEV],
+    "bwd_postprocess": ["exact_attention_fa_amd/csrc/fa_bwd.hip", *_DEV],
 }
 
 

@@ -41,9 +41,15 @@ def common_flags():
     ]
 
 
+# Per-source device-code options.  The backward's MFMA results (scores and dP) feed VALU work,
+# which cannot read accumulation registers: the VGPR form of the MFMAs saves the copies out of
+# them (measured: dK/dV pass 6% fewer cycles; no other kernel changes).
+DEVICE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, resource_usage: bool) -> tuple[str, str]:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *DEVICE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if resource_usage and src.endswith(".hip"):
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     p = subprocess.run(cmd, capture_output=True, text=True)
