@@ -43,7 +43,8 @@ constexpr int kBwdBQ = 64;    // query rows per streamed tile
 constexpr int kDqBC = 32;     // dQ kernel: keys per K/V tile
 
 // ---------------------------------------------------------------- preprocess
-// D[row] = sum_d dO[row][d] * O[row][d] (fp32) and L2[row] = LSE[row] * log2(e) (the
+// Dl[row] = -D[row] = -sum_d dO[row][d] * O[row][d] (fp32, stored negated: it is the
+// accumulator input of the dK/dV pass's dP MFMAs) and L2[row] = LSE[row] * log2(e) (the
 // exponent offset of the base-2 recompute of P).
 template <typename TR, int HD>
 __global__ void __launch_bounds__(kThreads)
@@ -66,7 +67,7 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) {
-    Dl[row] = acc;
+    Dl[row] = -acc;
     L2[row] = LSE[row] * kLog2e;
   }
 }
@@ -206,34 +207,37 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // LSE*log2(e) and D of the unit's queries as this lane's registers see them:
-  // l[t2*2 + h][e] is query qb*32 + t2*16 + g*8 + h*4 + e.
+  // Per-query values of a unit as this lane's accumulator registers see them: register i is
+  // query qb*32 + (i/8)*16 + g*8 + i%8, so four 16-byte reads give all sixteen in order.
+  // LSE*log2(e) feeds P; -D (stored negated by the preprocess) is the accumulator input of the
+  // dP MFMAs, which then produce dP - D directly.
   struct RowVals {
-    f32x4 l[4], d[4];
+    f32x4 l[4];
   };
   auto rowvals = [&](const char* sl, int qb) FA_INL {
     RowVals r;
     const float* tL = reinterpret_cast<const float*>(sl + OFF_L);
-    const float* tD = reinterpret_cast<const float*>(sl + OFF_D);
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int q = qb * 32 + t2 * 16 + g * 8 + h * 4;
-        r.l[t2 * 2 + h] = *reinterpret_cast<const f32x4*>(tL + q);
-        r.d[t2 * 2 + h] = *reinterpret_cast<const f32x4*>(tD + q);
-      }
+    for (int t = 0; t < 4; ++t) r.l[t] = *reinterpret_cast<const f32x4*>(tL + qb * 32 + (t >> 1) * 16 + g * 8 + (t & 1) * 4);
     return r;
   };
+  auto neg_d = [&](const char* sl, int qb) FA_INL {
+    const float* tD = reinterpret_cast<const float*>(sl + OFF_D);
+    f32x4 d[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) d[t] = *reinterpret_cast<const f32x4*>(tD + qb * 32 + (t >> 1) * 16 + g * 8 + (t & 1) * 4);
+    return f32x16{d[0][0], d[0][1], d[0][2], d[0][3], d[1][0], d[1][1], d[1][2], d[1][3],
+                  d[2][0], d[2][1], d[2][2], d[2][3], d[3][0], d[3][1], d[3][2], d[3][3]};
+  };
   // P = exp2(S c2 - LSE log2 e) and dS = P (dP - D) of one unit as 16 work units (one query
-  // register each), packed into the A operands of dV += P^T dO and dK += dS^T Q.
+  // register each; dp already holds dP - D), packed into the A operands of dV += P^T dO and
+  // dK += dS^T Q.
   auto pds_unit = [&](f32x16& s, const f32x16& dp, const RowVals& rv, u32x4 (&pa)[2], u32x4 (&dsa)[2],
                       float (&pt)[2], float (&dt)[2], int i) FA_INL {
     const int t2 = i >> 3, j = i & 7;
     const float lse2 = rv.l[t2 * 2 + (j >> 2)][j & 3];
-    const float dd = rv.d[t2 * 2 + (j >> 2)][j & 3];
     const float p = fast_exp2(fmaf(s[i], c2, -lse2));
-    const float ds = p * (dp[i] - dd);
+    const float ds = p * dp[i];
     if (j & 1) {
       pa[t2][j >> 1] = TR::pack(pt[0], p);
       dsa[t2][j >> 1] = TR::pack(dt[0], ds);
@@ -291,7 +295,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     float pt[2], dt[2];
     if constexpr (HAS_NEXT) {
       ns = f32x16{};
-      ndp = f32x16{};
+      ndp = neg_d(nsl, qb ^ 1);
       sdp(nsl, qb ^ 1, ns, ndp, [&](int i) FA_INL {
 #pragma unroll
         for (int w = 0; w < 16; ++w)
@@ -328,7 +332,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     wait_vmcnt<0>();
     lds_barrier();
     s0 = f32x16{};
-    dp0 = f32x16{};
+    dp0 = neg_d(smem, 0);
     sdp(smem, 0, s0, dp0, [](int) FA_INL {});
     char* c0 = smem;
     char* c1 = smem + SLOT;
@@ -483,7 +487,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     of[kk] = ld16_if(dO + rowoff + kk * 16 + g * 8, qi < N);
   }
   const float l2 = qi < N ? L2[(size_t)bh * N + qi] : 0.f;
-  const float dd = qi < N ? Dl[(size_t)bh * N + qi] : 0.f;
+  const float nd = qi < N ? Dl[(size_t)bh * N + qi] : 0.f;  // -D
 
   const uint32_t koff[2] = {sl_off<BC>(perm_rows(c), g * 8), sl_off<BC>(perm_rows(c), 16 + g * 8)};
   const TrLane trl = tr_lane(lane);
@@ -528,7 +532,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const int key = (t0 + j) * BC + (i >> 3) * 16 + g * 8 + (i & 7);
       if (key > qi) sv = -INFINITY;
     }
-    const float ds = fast_exp2(fmaf(sv, c2, -l2)) * (dp[i] - dd);
+    const float ds = fast_exp2(fmaf(sv, c2, -l2)) * (dp[i] + nd);
     if (i & 1)
       dsb[i >> 3][(i & 7) >> 1] = TR::pack(dt, ds);
     else

@@ -38,7 +38,7 @@ struct MergeArgs {
 
 // Workspace carve-up used by the backward stages (byte offsets from the base).
 struct BwdWorkspace {
-  size_t delta;    // fp32 (B, Hq, N): D = rowsum(dO * O)
+  size_t delta;    // fp32 (B, Hq, N): -D = -rowsum(dO * O)
   size_t lse2;     // fp32 (B, Hq, N): LSE * log2(e)
   size_t dk_part;  // fp32 (B, Hq, n_qp, N, D): dK partials per query head and query-range piece
   size_t dv_part;  // fp32 (B, Hq, n_qp, N, D): dV partials (both only when partial_dkdv)

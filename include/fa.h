@@ -151,7 +151,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * between them.  Running them in this order on one stream with the same workspace is
  * exactly fa_bwd (fa_bwd_dkdv and fa_bwd_dq only depend on the preprocess and may run in
  * either order).
- *   fa_bwd_preprocess:  D = rowsum(dout * o) and LSE * log2(e) into the workspace (fp32).
+ *   fa_bwd_preprocess:  -D = -rowsum(dout * o) and LSE * log2(e) into the workspace (fp32).
  *   fa_bwd_dkdv:        key-stationary pass: recomputes P from the workspace's LSE and
  *                       writes dk = scale * dS^T Q and dv = P^T dO (Hq == Hkv), or fp32
  *                       per-query-head partials into the workspace (Hq > Hkv).
