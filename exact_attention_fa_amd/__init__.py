@@ -11,7 +11,8 @@ The functions carry the C entry points' names:
     dq, dk, dv = fa_bwd(q, k, v, o, do, lse, causal=False, softmax_scale=None)
 
 q: (B, Hq, N, D), k and v: (B, Hkv, N, D), contiguous CUDA(HIP) tensors of dtype
-torch.float16 or torch.bfloat16, D in {64, 128}, Hq a multiple of Hkv.
+torch.float16 or torch.bfloat16 (or torch.float32 for the fp32 verification path of
+fa_fwd and fa_bwd), D in {64, 128}, Hq a multiple of Hkv.
 """
 from __future__ import annotations
 
@@ -24,11 +25,12 @@ __all__ = [
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_size",
     "fa_merge_partials", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_postprocess",
     "fa_bwd_workspace_size", "fa_version", "fa_status_string", "library_path", "load_library",
-    "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16",
+    "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16", "FA_FP32",
 ]
 
 FA_FP16 = 0
 FA_BF16 = 1
+FA_FP32 = 2
 _LIB_NAME = "libfa_mi355x.so"
 _lock = threading.Lock()
 _lib = None
@@ -106,7 +108,9 @@ def _dtype_code(t):
         return FA_FP16
     if t.dtype == torch.bfloat16:
         return FA_BF16
-    raise RuntimeError(f"unsupported dtype {t.dtype}: float16 or bfloat16 only")
+    if t.dtype == torch.float32:
+        return FA_FP32  # the fp32 verification path (fa_fwd, fa_bwd and its stages)
+    raise RuntimeError(f"unsupported dtype {t.dtype}: float16, bfloat16 or float32 only")
 
 
 def _dims(q, k, v):

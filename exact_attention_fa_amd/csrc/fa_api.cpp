@@ -28,7 +28,11 @@ int check_dims(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D) {
   return FA_OK;
 }
 
-int check_dtype(int dtype) { return (dtype == FA_FP16 || dtype == FA_BF16) ? FA_OK : FA_ERR_DTYPE; }
+int check_dtype(int dtype) {
+  return (dtype == FA_FP16 || dtype == FA_BF16 || dtype == FA_FP32) ? FA_OK : FA_ERR_DTYPE;
+}
+int check_dtype16(int dtype) { return (dtype == FA_FP16 || dtype == FA_BF16) ? FA_OK : FA_ERR_DTYPE; }
+size_t elem_size(int dtype) { return dtype == FA_FP32 ? 4 : 2; }
 
 int check_scale(float s) { return (isfinite(s) && s >= 0.f) ? FA_OK : FA_ERR_SCALE; }
 
@@ -108,7 +112,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_BAD_SHAPE: return "B, Hq, Hkv and N must be positive";
     case FA_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
     case FA_ERR_GQA: return "Hq must be a multiple of Hkv";
-    case FA_ERR_DTYPE: return "dtype must be FA_FP16 or FA_BF16";
+    case FA_ERR_DTYPE: return "dtype must be FA_FP16 or FA_BF16 (or FA_FP32 for fa_fwd, fa_bwd and its stages)";
     case FA_ERR_SCALE: return "softmax_scale must be finite and >= 0";
     case FA_ERR_ALIGNMENT: return "buffers must be 16-byte aligned (lse: 4-byte)";
     case FA_ERR_WORKSPACE: return "workspace is smaller than fa_bwd_workspace_size()";
@@ -130,12 +134,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   FA_TRY(check_ptr(v, 16));
   FA_TRY(check_ptr(o, 16));
   FA_TRY(check_ptr(lse, 4));
-  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const size_t qb = (size_t)(B * Hq * N * D) * elem_size(dtype), kb = (size_t)(B * Hkv * N * D) * elem_size(dtype);
   const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {o, qb, true},
                      {lse, (size_t)(B * Hq * N) * 4, true}};
   FA_TRY(check_alias(r, 5));
   FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, D, softmax_scale, causal != 0, dtype == FA_BF16,
             static_cast<hipStream_t>(stream)};
+  a.f32 = dtype == FA_FP32;
   return status_of(launch_fwd(a));
 }
 
@@ -158,7 +163,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   FA_TRY(check_dims(B, Hq, Hkv, N, D));
   FA_TRY(check_scale(softmax_scale));
   if (n_split < 0 || n_split > kMaxParts) return FA_ERR_SPLIT;
-  const int n = n_split == 0 ? fwd_auto_parts(B, Hq, N, D, causal != 0) : n_split;
+  // the fp32 path has no pieces: any count resolves to fa_fwd
+  const int n = dtype == FA_FP32 ? 1 : (n_split == 0 ? fwd_auto_parts(B, Hq, N, D, causal != 0) : n_split);
   if (n == 1) return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, D, softmax_scale, causal, dtype, stream);
   FA_TRY(check_ptr(q, 16));
   FA_TRY(check_ptr(k, 16));
@@ -169,14 +175,14 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   const size_t need = fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, n);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
   const size_t rows = (size_t)(B * Hq * N);
-  const size_t qb = rows * (size_t)D * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const size_t qb = rows * (size_t)D * 2, kb = (size_t)(B * Hkv * N * D) * 2;  // 16-bit here
   const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {o, qb, true}, {lse, rows * 4, true},
                      {workspace, need, true}};
   FA_TRY(check_alias(r, 6));
   float* const op = static_cast<float*>(workspace);
   float* const lp = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((size_t)n * rows * D * 4));
   FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, D, softmax_scale, causal != 0, dtype == FA_BF16,
-            static_cast<hipStream_t>(stream), n, op, lp};
+            static_cast<hipStream_t>(stream), false, n, op, lp};
   FA_TRY(status_of(launch_fwd(a)));
   const MergeArgs m{op, lp, n, (long long)rows, D, o, lse, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
   return status_of(launch_merge(m));
@@ -184,7 +190,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 
 int fa_merge_partials(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int64_t rows,
                       int64_t D, int dtype, void* stream) {
-  FA_TRY(check_dtype(dtype));
+  FA_TRY(check_dtype16(dtype));
   if (rows <= 0) return FA_ERR_BAD_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (n_parts < 1 || n_parts > kMaxParts) return FA_ERR_SPLIT;
@@ -221,8 +227,10 @@ int check_bwd_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, i
 BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, void* ws, int64_t B, int64_t Hq,
                       int64_t Hkv, int64_t N, int64_t D, float scale, int causal, int dtype, void* stream) {
-  return BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, static_cast<char*>(ws), B, Hq, Hkv, N, D, scale,
-                 causal != 0, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
+  BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<char*>(ws), B, Hq, Hkv, N, D, scale,
+            causal != 0, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
+  a.f32 = dtype == FA_FP32;
+  return a;
 }
 
 }  // namespace
@@ -235,7 +243,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const void* p16[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : p16) FA_TRY(check_ptr(p, 16));
   FA_TRY(check_ptr(lse, 4));
-  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const size_t qb = (size_t)(B * Hq * N * D) * elem_size(dtype), kb = (size_t)(B * Hkv * N * D) * elem_size(dtype);
   const Range r[] = {{q, qb, false},  {k, kb, false},  {v, kb, false},  {o, qb, false},
                      {dout, qb, false}, {lse, (size_t)(B * Hq * N) * 4, false},
                      {dq, qb, true},  {dk, kb, true},  {dv, kb, true},
@@ -255,7 +263,7 @@ int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* w
   FA_TRY(check_ptr(o, 16));
   FA_TRY(check_ptr(dout, 16));
   FA_TRY(check_ptr(lse, 4));
-  const size_t qb = (size_t)(B * Hq * N * D) * 2;
+  const size_t qb = (size_t)(B * Hq * N * D) * elem_size(dtype);
   const Range r[] = {{o, qb, false}, {dout, qb, false}, {lse, (size_t)(B * Hq * N) * 4, false},
                      {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, true}};
   FA_TRY(check_alias(r, 4));
@@ -271,12 +279,13 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, v
   FA_TRY(check_scale(softmax_scale));
   const void* p16[] = {q, k, v, dout};
   for (const void* p : p16) FA_TRY(check_ptr(p, 16));
-  const bool direct = !bwd_workspace_layout(B, Hq, Hkv, N, D).partial_dkdv;
+  // the fp32 path writes dk/dv directly; the 16-bit path writes partials for GQA and pieces
+  const bool direct = dtype == FA_FP32 || !bwd_workspace_layout(B, Hq, Hkv, N, D).partial_dkdv;
   if (direct) {
     FA_TRY(check_ptr(dk, 16));
     FA_TRY(check_ptr(dv, 16));
   }
-  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const size_t qb = (size_t)(B * Hq * N * D) * elem_size(dtype), kb = (size_t)(B * Hkv * N * D) * elem_size(dtype);
   const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {dout, qb, false},
                      {direct ? dk : nullptr, kb, true}, {direct ? dv : nullptr, kb, true},
                      {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, !direct}};
@@ -293,10 +302,10 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
   FA_TRY(check_scale(softmax_scale));
   const void* p16[] = {q, k, v, dout, dq};
   for (const void* p : p16) FA_TRY(check_ptr(p, 16));
-  const size_t qb = (size_t)(B * Hq * N * D) * 2, kb = (size_t)(B * Hkv * N * D) * 2;
+  const size_t qb = (size_t)(B * Hq * N * D) * elem_size(dtype), kb = (size_t)(B * Hkv * N * D) * elem_size(dtype);
   const BwdWorkspace w = bwd_workspace_layout(B, Hq, Hkv, N, D);
   const Range r[] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {dout, qb, false}, {dq, qb, true},
-                     {workspace, w.total, w.n_kp > 1}};
+                     {workspace, w.total, w.n_kp > 1 && dtype != FA_FP32}};
   FA_TRY(check_alias(r, 6));
   const BwdArgs a = make_bwd_args(q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, D,
                                   softmax_scale, causal, dtype, stream);
@@ -308,7 +317,7 @@ int fa_bwd_postprocess(void* dk, void* dv, void* workspace, size_t workspace_byt
   FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
   FA_TRY(check_ptr(dk, 16));
   FA_TRY(check_ptr(dv, 16));
-  const size_t kb = (size_t)(B * Hkv * N * D) * 2;
+  const size_t kb = (size_t)(B * Hkv * N * D) * elem_size(dtype);
   const Range r[] = {{dk, kb, true}, {dv, kb, true},
                      {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, false}};
   FA_TRY(check_alias(r, 3));

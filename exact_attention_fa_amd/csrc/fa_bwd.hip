@@ -867,18 +867,24 @@ int bwd_key_pieces(long long B, long long Hq, long long N, long long D) {
 }
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a) {
+  if (a.f32) return launch_bwd_preprocess_f32(a);
   if (a.bf16) return a.D == 64 ? pre_t<Bf16, 64>(a) : pre_t<Bf16, 128>(a);
   return a.D == 64 ? pre_t<F16, 64>(a) : pre_t<F16, 128>(a);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+  if (a.f32) return launch_bwd_dkdv_f32(a);
   if (a.bf16) return a.D == 64 ? dkdv_hd<Bf16, 64>(a) : dkdv_hd<Bf16, 128>(a);
   return a.D == 64 ? dkdv_hd<F16, 64>(a) : dkdv_hd<F16, 128>(a);
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a) { return a.bf16 ? dq_dt<Bf16>(a) : dq_dt<F16>(a); }
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  if (a.f32) return launch_bwd_dq_f32(a);
+  return a.bf16 ? dq_dt<Bf16>(a) : dq_dt<F16>(a);
+}
 
 hipError_t launch_bwd_postprocess(const BwdArgs& a) {
+  if (a.f32) return hipSuccess;  // the fp32 dK/dV pass writes dk/dv directly
   return a.bf16 ? post_t<Bf16>(a) : post_t<F16>(a);
 }
 

@@ -617,6 +617,7 @@ hipError_t launch_merge_t(const MergeArgs& a) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.f32) return launch_fwd_f32(a);
   if (a.n_part > 1) return a.bf16 ? launch_fwd_part_dt<Bf16>(a) : launch_fwd_part_dt<F16>(a);
   return a.bf16 ? launch_fwd_dt<Bf16>(a) : launch_fwd_dt<F16>(a);
 }

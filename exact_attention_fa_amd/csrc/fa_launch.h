@@ -19,6 +19,7 @@ struct FwdArgs {
   bool causal;
   bool bf16;
   hipStream_t stream;
+  bool f32 = false;          // float32 tensors (the fp32 verification path; bf16 is ignored)
   int n_part = 1;            // > 1: key-range pieces written as fp32 partials (o_part, lse_part)
   float* o_part = nullptr;   // (n_part, B, Hq, N, D)
   float* lse_part = nullptr; // (n_part, B, Hq, N)
@@ -69,6 +70,7 @@ struct BwdArgs {
   bool causal;
   bool bf16;
   hipStream_t stream;
+  bool f32 = false;  // float32 tensors (the fp32 verification path)
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
@@ -78,5 +80,11 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_postprocess(const BwdArgs& a);
+// The fp32 verification path (fa_f32.hip); launch_fwd and the launch_bwd_* stages dispatch to
+// these when FwdArgs::f32 / BwdArgs::f32 is set.
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_preprocess_f32(const BwdArgs& a);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a);
+hipError_t launch_bwd_dq_f32(const BwdArgs& a);
 
 }  // namespace fa

@@ -14,7 +14,7 @@ from dataclasses import dataclass
 
 import torch
 
-DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}
 
 
 @dataclass(frozen=True)

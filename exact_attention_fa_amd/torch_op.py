@@ -70,7 +70,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
               softmax_scale: Optional[float] = None) -> torch.Tensor:
     """Exact softmax attention O = softmax(scale * Q K^T [causal mask]) V, differentiable.
 
-    q: (B, Hq, N, D), k, v: (B, Hkv, N, D), contiguous, float16 or bfloat16, on the GPU;
+    q: (B, Hq, N, D), k, v: (B, Hkv, N, D), contiguous, float16 or bfloat16 (float32 runs the
+    fp32 verification path), on the GPU;
     D in {64, 128}; Hq a multiple of Hkv; scale defaults to 1/sqrt(D).
     """
     scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)

@@ -24,7 +24,13 @@
  *              the same for queries and keys (self-attention).
  *   dtype      FA_FP16 or FA_BF16 for every 16-bit tensor of a call; LSE, the backward
  *              workspace and all accumulation are fp32.  Outputs are rounded to nearest
- *              even.
+ *              even.  FA_FP32 selects the float32 verification path for fa_fwd, fa_bwd and
+ *              the fa_bwd stages: every tensor float32, products and sums in fp32 FMAs
+ *              ("FlashAttention for Tesla P100", section "What it supports": fp32
+ *              accumulation; "FlashNystrom", section "Scope": an fp32 path kept for
+ *              gradient checking).  It is plain and correct rather than fast (no matrix
+ *              cores), for checking the 16-bit results against.  fa_fwd_splitkv runs it
+ *              as fa_fwd; fa_merge_partials does not take it.
  *   Heads      Hq must be a multiple of Hkv; query head h reads KV head h / (Hq / Hkv)
  *              (MHA, GQA and MQA).
  *   Causal     causal != 0: key j is visible to query i iff j <= i (square, top-left).
@@ -56,7 +62,8 @@ extern "C" {
 
 enum fa_dtype {
   FA_FP16 = 0,
-  FA_BF16 = 1
+  FA_BF16 = 1,
+  FA_FP32 = 2  /* float32 verification path: fa_fwd, fa_bwd and its stages only */
 };
 
 enum fa_status {
@@ -65,7 +72,7 @@ enum fa_status {
   FA_ERR_BAD_SHAPE = 2,    /* B, Hq, Hkv or N <= 0 */
   FA_ERR_HEAD_DIM = 3,     /* D is not 64 or 128 */
   FA_ERR_GQA = 4,          /* Hq is not a multiple of Hkv */
-  FA_ERR_DTYPE = 5,        /* dtype is not FA_FP16 / FA_BF16 */
+  FA_ERR_DTYPE = 5,        /* dtype is not FA_FP16 / FA_BF16 (/ FA_FP32 where accepted) */
   FA_ERR_SCALE = 6,        /* softmax_scale is negative, NaN or infinite */
   FA_ERR_ALIGNMENT = 7,    /* a pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = 8,    /* workspace_bytes < fa_bwd_workspace_size(...) */

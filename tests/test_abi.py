@@ -74,7 +74,7 @@ def fwd(lib, q=0, k=1, v=2, o=3, l=4, B=1, Hq=2, Hkv=2, N=256, D=64, scale=0.125
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=2), "FA_ERR_DTYPE"),
+    (dict(dtype=3), "FA_ERR_DTYPE"),
     (dict(dtype=-1), "FA_ERR_DTYPE"),
     (dict(B=0), "FA_ERR_BAD_SHAPE"),
     (dict(Hq=0), "FA_ERR_BAD_SHAPE"),
@@ -122,6 +122,14 @@ def bwd(lib, ws_bytes=None, B=1, Hq=2, Hkv=2, N=256, D=64, scale=0.125, dtype=0,
     if ws_bytes is None:
         ws_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D)
     return lib.fa_bwd(*[ptrs[n] for n in names], ws_bytes, B, Hq, Hkv, N, D, scale, 0, dtype, None)
+
+
+def test_fp32_sizes_in_alias_checks(lib):
+    # float32 buffers are twice as long: o right after q's 16-bit extent overlaps q in fp32
+    B, Hq, N, D = 1, 2, 256, 64
+    q16 = B * Hq * N * D * 2
+    qp, op = ctypes.c_void_p(A), ctypes.c_void_p(A + q16)
+    assert fwd(lib, q=qp, o=op, dtype=2) == STATUS["FA_ERR_ALIAS"]
 
 
 def test_bwd_rejects(lib):
@@ -215,6 +223,7 @@ def test_merge_rejects(lib):
     assert merge(rows=0) == STATUS["FA_ERR_BAD_SHAPE"]
     assert merge(D=32) == STATUS["FA_ERR_HEAD_DIM"]
     assert merge(dtype=3) == STATUS["FA_ERR_DTYPE"]
+    assert merge(dtype=2) == STATUS["FA_ERR_DTYPE"]  # the fp32 path has no pieces to merge
     assert merge(op=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]
     assert merge(op=ctypes.c_void_p(A + 4)) == STATUS["FA_ERR_ALIGNMENT"]
     assert merge(o=0) == STATUS["FA_ERR_ALIAS"]
