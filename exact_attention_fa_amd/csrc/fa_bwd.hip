@@ -231,12 +231,19 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   // P = exp2(S c2 - LSE log2 e) and dS = P (dP - D) of one unit as 16 work units (one query
   // register each; dp already holds dP - D), packed into the A operands of dV += P^T dO and
-  // dK += dS^T Q.
-  auto pds_unit = [&](f32x16& s, const f32x16& dp, const RowVals& rv, u32x4 (&pa)[2], u32x4 (&dsa)[2],
-                      float (&pt)[2], float (&dt)[2], int i) FA_INL {
+  // dK += dS^T Q.  A unit runs in three stages, each on its own register of s (the exponent,
+  // then P, then dS and the packing), so that consecutive MFMA steps can carry stages of
+  // different units: with one wave per SIMD, a dependent chain inside one step would stall
+  // the in-order issue.
+  auto pds_a = [&](f32x16& s, const RowVals& rv, int i) FA_INL {
     const int t2 = i >> 3, j = i & 7;
-    const float lse2 = rv.l[t2 * 2 + (j >> 2)][j & 3];
-    const float p = fast_exp2(fmaf(s[i], c2, -lse2));
+    s[i] = fmaf(s[i], c2, -rv.l[t2 * 2 + (j >> 2)][j & 3]);
+  };
+  auto pds_b = [&](f32x16& s, int i) FA_INL { s[i] = fast_exp2(s[i]); };
+  auto pds_c = [&](f32x16& s, const f32x16& dp, u32x4 (&pa)[2], u32x4 (&dsa)[2], float (&pt)[2], float (&dt)[2],
+                   int i) FA_INL {
+    const int t2 = i >> 3, j = i & 7;
+    const float p = s[i];
     const float ds = p * dp[i];
     if (j & 1) {
       pa[t2][j >> 1] = TR::pack(pt[0], p);
@@ -296,14 +303,24 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if constexpr (HAS_NEXT) {
       ns = f32x16{};
       ndp = neg_d(nsl, qb ^ 1);
+      // unit w finishes at MFMA step h = w * 2 * KST / 16; its exponent and exp2 run one and
+      // two steps earlier (clamped to the first step)
       sdp(nsl, qb ^ 1, ns, ndp, [&](int i) FA_INL {
 #pragma unroll
-        for (int w = 0; w < 16; ++w)
-          if (w * 2 * KST / 16 == i) pds_unit(cs, cdp, rv, pa, dsa, pt, dt, w);
+        for (int w = 0; w < 16; ++w) {
+          const int h = w * 2 * KST / 16;  // (a unit's stages in order when clamped together)
+          if ((h >= 2 ? h - 2 : 0) == i) pds_a(cs, rv, w);
+          if ((h >= 1 ? h - 1 : 0) == i) pds_b(cs, w);
+          if (h == i) pds_c(cs, cdp, pa, dsa, pt, dt, w);
+        }
       });
     } else {
 #pragma unroll
-      for (int w = 0; w < 16; ++w) pds_unit(cs, cdp, rv, pa, dsa, pt, dt, w);
+      for (int w = 0; w < 16; ++w) pds_a(cs, rv, w);
+#pragma unroll
+      for (int w = 0; w < 16; ++w) pds_b(cs, w);
+#pragma unroll
+      for (int w = 0; w < 16; ++w) pds_c(cs, cdp, pa, dsa, pt, dt, w);
     }
     dvdk(sl, qb, pa, dsa);
   };
