@@ -101,6 +101,29 @@ BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long
 
 using namespace fa;
 
+namespace {
+
+// Validation common to the backward entry points; pointers are checked by the callers.
+int check_bwd_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
+                     const void* ws, size_t ws_bytes) {
+  FA_TRY(check_dtype(dtype));
+  FA_TRY(check_dims(B, Hq, Hkv, N, D));
+  FA_TRY(check_ptr(ws, 16));
+  if (ws_bytes < bwd_workspace_layout(B, Hq, Hkv, N, D).total) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, void* ws, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t N, int64_t D, float scale, int causal, int dtype, void* stream) {
+  BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<char*>(ws), B, Hq, Hkv, N, D, scale,
+            causal != 0, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
+  a.f32 = dtype == FA_FP32;
+  return a;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_version(void) { return kVersion; }
@@ -212,28 +235,6 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
   return bwd_workspace_layout(B, Hq, Hkv, N, D).total;
 }
 
-namespace {
-
-// Validation common to the backward entry points; pointers are checked by the callers.
-int check_bwd_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
-                     const void* ws, size_t ws_bytes) {
-  FA_TRY(check_dtype(dtype));
-  FA_TRY(check_dims(B, Hq, Hkv, N, D));
-  FA_TRY(check_ptr(ws, 16));
-  if (ws_bytes < bwd_workspace_layout(B, Hq, Hkv, N, D).total) return FA_ERR_WORKSPACE;
-  return FA_OK;
-}
-
-BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv, void* ws, int64_t B, int64_t Hq,
-                      int64_t Hkv, int64_t N, int64_t D, float scale, int causal, int dtype, void* stream) {
-  BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<char*>(ws), B, Hq, Hkv, N, D, scale,
-            causal != 0, dtype == FA_BF16, static_cast<hipStream_t>(stream)};
-  a.f32 = dtype == FA_FP32;
-  return a;
-}
-
-}  // namespace
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq,

@@ -10,16 +10,19 @@
 // below the diagonal ("FlashAttention for Tesla P100", section "What it supports").
 //
 // gfx950 realisation:
-//   * 256 threads = 4 waves; a wave owns 32 query rows (BR = 128 rows per workgroup).
-//   * K/V tiles of BC = 64 keys are copied global -> LDS by direct loads into a double
-//     buffer, one tile ahead of the compute, with no register staging.
+//   * A wave owns 32 query rows; workgroups of 8 waves (256 rows, or 128 rows split over
+//     two wave groups that take halves of the key range) or of 4 waves (128 rows).
+//   * K/V tiles of BC = 64 keys are copied global -> LDS by direct loads into rings of
+//     buffers, one or two tiles ahead of the compute, with no register staging.
 //   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16: each lane then
 //     owns one query column, its row max and row sum are in-lane reductions plus one
 //     v_permlane32_swap, and the bf16/fp16-rounded probabilities in registers are already
 //     the B operand of O^T += V^T P^T.  V^T comes from the row-major V tile through
 //     ds_read_b64_tr_b16.
-//   * exp2 on the VALU with scale*log2(e) folded into one FMA per score; the running max
-//     is moved (and O, l rescaled) only when it grows by more than 2^8.
+//   * exp2 on the VALU with scale*log2(e) folded into one FMA per score.  The first tile
+//     sets a reference max; later tiles form probabilities against it without a max, since
+//     their row sum bounds each of them, and a rare tile over the bound is recomputed with
+//     the reference moved.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -76,15 +79,13 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // workgroup per CU has LDS to spare for two steps of lead; two 4-wave workgroups share a
   // CU and keep one, and so do the two groups of a split workgroup.
   constexpr int DIST = (NW == 8 && SPLIT == 1) ? 2 : 1, NB = DIST + 1;
-  // SUMCHK: the running max is not tracked per tile.  Probabilities are formed against the
-  // reference max, and the row sum, computed anyway, bounds every one of them: while a lane's
-  // share of the tile's sum stays <= 2^7, no probability exceeds 2^8 and nothing needs to be
-  // rescaled.  Otherwise (rare: a score far above the reference) the tile's scores are
-  // recomputed from its K tile, still resident in a fourth K buffer, and handled exactly as
-  // the tracked-max path would.  This takes the 16 v_max3 and the cross-lane reduction per
-  // tile off the VALU.
-  constexpr bool SUMCHK = true;
-  constexpr int NBK = SUMCHK ? NB + 1 : NB;
+  // The running max is not tracked per tile.  Probabilities are formed against the reference
+  // max, and the row sum, computed anyway, bounds every one of them: while a lane's share of
+  // the tile's sum stays <= 2^7, no probability exceeds 2^8 and nothing needs to be rescaled.
+  // Otherwise (rare: a score far above the reference) the tile's scores are recomputed from
+  // its K tile, still resident in one more K buffer, and the reference moves to their max.
+  // This takes the 16 v_max3 and the cross-lane reduction per tile off the VALU.
+  constexpr int NBK = NB + 1;
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * (NBK + NB) * TILE];  // per group: K[NBK], V[NB]
 
   const int tid = threadIdx.x;
@@ -239,11 +240,10 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
   };
   // Online softmax in raw-score units (c2 = scale * log2(e) > 0), as units u of work (see
-  // sm_step).  The reference max moves only when the tile max exceeds it by more than
-  // 2^kRescaleLog2 in the exp2 domain (always on the first tile); otherwise probabilities up
-  // to 2^kRescaleLog2 accumulate against the stale reference, exact because O and l share
-  // it.  When it moves, O is scaled by alpha at the start of the next step, after the P V
-  // products issued in this step.
+  // sm_step).  The full set (maxima, reduction, exp2) runs on a wave's first tile, where the
+  // reference max is set (kRescaleLog2 only decides whether it moves there; it always does
+  // from -inf); the steady steps run the exp2 units alone (see check / redo).  When the
+  // reference moves, O is scaled by alpha before the next P V.
   bool need = false;  // uniform: O must be scaled by alpha before the next P V
   float alpha = 1.f;
   float mx0 = 0.f, mx1 = 0.f, mb = 0.f;
@@ -292,7 +292,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // and/or P_{j-1} V_{j-1}.  The LDS buffers are restrict-qualified parameters so that the
   // compiler can tell these reads from the direct loads in flight and does not make them wait.
   enum Kind { kFirst, kFirstMasked, kSteady, kSteadyMasked, kDrain, kIdle };
-  // The rare path of SUMCHK: P_{jp} (the previous tile, its K tile in tKp) is recomputed with
+  // The rare path: P_{jp} (the previous tile, its K tile in tKp) is recomputed with
   // the reference moved to the tile's max; l is rescaled here and O (flagged by `need`) just
   // before P_{jp} V_{jp} is added.
   auto redo = [&](const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2]) FA_INL {
@@ -320,13 +320,11 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int i = 0; i < 16; ++i) pack_unit(pb, i);
   };
   auto check = [&](const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2]) FA_INL {
-    if constexpr (SUMCHK) {
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= 0x1p7f)) != 0, 0)) redo(tKp, jp, pb);
-      if (need) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= 0x1p7f)) != 0, 0)) redo(tKp, jp, pb);
+    if (need) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        need = false;
-      }
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      need = false;
     }
   };
 
@@ -360,17 +358,12 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       f32x16 s[2] = {f32x16{}, f32x16{}};
       u32x4 pb[2][2];
       rs = 0.f;
-      // Without masks, the first block's maxima (units 0..7) run in the second half of the
-      // S MFMAs; a masked tile takes all of them after the mask.  SUMCHK runs the exp2 units
-      // only (FIRST = kSmExp0).
-      constexpr int NS = 2 * KST, EARLY = (KIND == kSteady && !SUMCHK) ? 8 : 0;
-      constexpr int FIRST = SUMCHK ? kSmExp0 : EARLY;
+      // The steady steps run only the exp2 units of the softmax (FIRST = kSmExp0); the masks
+      // of a masked tile come after its S MFMAs.
+      constexpr int NS = 2 * KST, FIRST = kSmExp0;
       scores(tK, s, [&](int i) FA_INL {
 #pragma unroll
         for (int u = i * 16 / NS; u < (i + 1) * 16 / NS; ++u) pack_unit(pb, u);
-#pragma unroll
-        for (int u = 0; u < EARLY; ++u)
-          if (KST + 1 + u * (NS - KST - 1) / EARLY == i) softmax_unit(s, u);
       });
       check(pK, j - 1, pb);
       l_run += rs;
@@ -402,8 +395,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // Buffer rings: step j reads K_j from kc and V_{j-1} from vp and fills kd with K_{j+DIST}
-  // and vd with V_{j+DIST-1}; with DIST = 2, kf holds K_{j+1} and vf holds V_j in flight, and
-  // kp keeps K_{j-1} (SUMCHK).
+  // and vd with V_{j+DIST-1}; with DIST = 2, kf holds K_{j+1} and vf holds V_j in flight; kp
+  // keeps K_{j-1} for the rare path.
   char* kc = sK;
   char* kf = sK + TILE;
   char* kd = sK + (NB - 1) * TILE;
@@ -414,17 +407,11 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto run = [&](auto kind_tag, int j) FA_INL {
     step(kind_tag, j, kd, vd, kc, vp, kp);
     char* t;
-    if constexpr (SUMCHK && DIST == 2) {
+    if constexpr (DIST == 2) {
       t = kp, kp = kc, kc = kf, kf = kd, kd = t;
       t = vp, vp = vf, vf = vd, vd = t;
-    } else if constexpr (SUMCHK) {
-      t = kp, kp = kc, kc = kd, kd = t;
-      t = vp, vp = vd, vd = t;
-    } else if constexpr (DIST == 2) {
-      t = kc, kc = kf, kf = kd, kd = t;
-      t = vp, vp = vf, vf = vd, vd = t;
     } else {
-      t = kc, kc = kd, kd = t;
+      t = kp, kp = kc, kc = kd, kd = t;
       t = vp, vp = vd, vd = t;
     }
   };
