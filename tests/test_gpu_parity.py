@@ -180,3 +180,33 @@ def test_causal_long_bf16_sampled():
     errs, _ = sampled_check(shape, workload_seed("causal_long_bf16", 0), units=[(0, 5)],
                             n_rows=48, backward=True)
     log("  errors", errs)
+
+
+def test_shard_causal_bf16_sampled():
+    """One GPU's share of the long causal workload (one head, N = 16384) in the launch
+    configuration bench.py times: fa_fwd_splitkv with the library's choice of key-range pieces,
+    then fa_bwd with its query- and key-range pieces; sampled rows and keys against the
+    oracle."""
+    import numpy as np
+    import torch
+    import exact_attention_fa_amd as fa
+    from parity_util import assert_fwd_close, assert_grad_close, attention_backward, attention_forward, f64
+    from exact_attention_fa_amd.inputs import make_inputs
+    shape = WORKLOADS["shard_causal_bf16"][0]
+    log("workload", shape)
+    B, Hq, Hkv, N, D = shape.B, shape.Hq, shape.Hkv, shape.N, shape.D
+    assert fa.fa_fwd_splitkv_parts(B, Hq, Hkv, N, D, True) > 1
+    q, k, v, do = (t.cuda() for t in make_inputs(shape, workload_seed("shard_causal_bf16", 0)))
+    o, lse = fa.fa_fwd_splitkv(q, k, v, causal=True)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    idx = np.unique(np.concatenate([[0, 127, 128, 8191, 16320, N - 1], rng.choice(N, 48, replace=False)]))
+    qs, ks, vs, dos = f64(q), f64(k), f64(v), f64(do)
+    o_r, l_r = attention_forward(qs, ks, vs, shape.scale, True, rows=idx)
+    errs = assert_fwd_close(f64(o)[:, :, idx], f64(lse)[:, :, idx], o_r, l_r, str(shape))
+    dq_r, dk_r, dv_r = attention_backward(qs, ks, vs, dos, shape.scale, True, rows=idx, keys=idx)
+    for name, g, r in (("dq", f64(dq)[:, :, idx], dq_r), ("dk", f64(dk)[:, :, idx], dk_r),
+                       ("dv", f64(dv)[:, :, idx], dv_r)):
+        assert_grad_close(g, r, name, str(shape))
+    log("  errors", errs)
