@@ -41,10 +41,13 @@ def common_flags():
     ]
 
 
-# Per-source device-code options.  The backward's MFMA results (scores and dP) feed VALU work,
-# which cannot read accumulation registers: the VGPR form of the MFMAs saves the copies out of
-# them (measured: dK/dV pass 6% fewer cycles; no other kernel changes).
-DEVICE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source device-code options.  MFMA results that feed VALU work (scores, dP) are wanted in
+# VGPRs, which the VALU reads directly, not in AGPRs, which it cannot: the compiler chooses the
+# AGPR form for every MFMA of a kernel that may use more than 256 VGPRs, so the VGPR form is
+# forced (measured: dK/dV pass 6% fewer cycles; no other kernel changes).  The forward's MFMAs
+# that accumulate in AGPRs are written as inline assembly.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+DEVICE_FLAGS = {"fa_bwd.hip": VGPR_FORM, "fa_fwd.hip": VGPR_FORM}
 
 
 def _compile(src: str, resource_usage: bool) -> tuple[str, str]:

@@ -10,8 +10,10 @@
 // below the diagonal ("FlashAttention for Tesla P100", section "What it supports").
 //
 // gfx950 realisation:
-//   * A wave owns 32 query rows; workgroups of 8 waves (256 rows, or 128 rows split over
-//     two wave groups that take halves of the key range) or of 4 waves (128 rows).
+//   * Large grids: workgroups of 4 waves that own 64 query rows each (256 rows, one wave
+//     per SIMD), so every K or V^T fragment read from LDS feeds two MFMAs.  Otherwise a wave
+//     owns 32 query rows, in workgroups of 8 waves (128 rows split over two wave groups that
+//     take halves of the key range) or of 4 waves (128 rows).
 //   * K/V tiles of BC = 64 keys are copied global -> LDS by direct loads into rings of
 //     buffers, one or two tiles ahead of the compute, with no register staging.
 //   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16: each lane then
@@ -35,19 +37,70 @@ namespace {
 constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 of the largest probability)
 
-// Work units of the softmax of one tile, in dependency order, spread over the MFMA steps
-// of the P V product they run under: 16 three-way maxima (weight 1 each), the cross-lane
-// reduction and reference update (weight 4), 32 fused scale-subtract + exp2 (weight 3 each).
+// Work units of the softmax of one tile and one 32-query block, in dependency order: 16
+// three-way maxima, the cross-lane reduction and reference update, 32 fused scale-subtract +
+// exp2.  With QB query blocks per wave, unit u belongs to block u % QB and is unit u / QB of
+// that block's list, so the blocks' chains interleave.
 constexpr int kSmMax = 16, kSmRed = 16, kSmExp0 = 17, kSmUnits = 49;
-constexpr int sm_weight(int u) { return u < kSmMax ? 1 : (u == kSmRed ? 4 : 3); }
-// Step (of nsteps) in whose share unit u >= first starts, for units [first, kSmUnits).
-constexpr int sm_step(int u, int nsteps, int first) {
-  int before = 0, total = 0;
-  for (int v = first; v < kSmUnits; ++v) {
-    if (v < u) before += sm_weight(v);
-    total += sm_weight(v);
-  }
-  return before * nsteps / total;
+
+// MFMAs for waves of 64 query rows.  Such a wave needs more than the 256 VGPRs, and the
+// compiler picks one register form for all MFMAs of a kernel, so these are written out: the
+// O accumulators (128 registers at D = 128) and the Q fragments (64) live in AGPRs, which only
+// MFMAs read, while the scores land in VGPRs, which the softmax reads directly.  The compiler
+// does not see these as MFMAs and inserts no wait states for them, so a sequence of them
+// carries its own (CDNA3/CDNA4 dependency rules): the first waits 2 for VALU writes of its
+// operands (s_nop 1), the last waits 24 (three s_nop 7) before anything else may touch a result
+// (an 8-pass XDL result needs at most 19 before a VALU or v_accvgpr access).  The waits are in
+// the same statement as the MFMA, so no instruction the compiler places around it can fall
+// inside the window.  Between them, A and B are read when an MFMA issues and an exactly
+// overlapping accumulator chains without wait states.
+enum { kNopNone, kNopBefore, kNopAfter };
+#define FA_MFMA_ASM(NOP, TEXT, OUT, ...)                                               \
+  do {                                                                                 \
+    if constexpr (NOP == kNopBefore)                                                   \
+      asm volatile("s_nop 1\n\t" TEXT : OUT : __VA_ARGS__);                            \
+    else if constexpr (NOP == kNopAfter)                                               \
+      asm volatile(TEXT "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : OUT : __VA_ARGS__);      \
+    else                                                                               \
+      asm volatile(TEXT : OUT : __VA_ARGS__);                                          \
+  } while (0)
+template <typename TR, int NOP>  // acc (AGPR) += a b
+__device__ __forceinline__ void mfma_av(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (std::is_same<TR, F16>::value)
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, %0", "+a"(acc), "v"(a), "v"(b));
+  else
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", "+a"(acc), "v"(a), "v"(b));
+}
+template <typename TR, int NOP>  // acc (VGPR) += a b (b in AGPRs)
+__device__ __forceinline__ void mfma_va(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (std::is_same<TR, F16>::value)
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, %0", "+v"(acc), "v"(a), "a"(b));
+  else
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", "+v"(acc), "v"(a), "a"(b));
+}
+template <typename TR, int NOP>  // acc (VGPR) = a b (b in AGPRs)
+__device__ __forceinline__ void mfma_va0(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (std::is_same<TR, F16>::value)
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, 0", "=&v"(acc), "v"(a), "a"(b));
+  else
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0", "=&v"(acc), "v"(a), "a"(b));
+}
+#undef FA_MFMA_ASM
+// Ordering point for the registers of `r`: each is an operand here, so no access to them
+// moves across it.  With `nop`, two wait states follow (after VALU or v_accvgpr writes of `r`,
+// before MFMAs read it).  The scheduler also keeps live ranges short around these points.
+template <typename T, int A, int B>
+__device__ __forceinline__ void reg_fence(T (&r)[A][B], bool agpr, bool nop) {
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (agpr)
+        asm volatile("" : "+a"(r[i][j]));
+      else
+        asm volatile("" : "+v"(r[i][j]));
+    }
+  if (nop) asm volatile("s_nop 1" ::: "memory");
 }
 
 // SPLIT = 2: the workgroup's waves form two groups that own the same query rows and split
@@ -60,25 +113,31 @@ constexpr int sm_step(int u, int nsteps, int first) {
 // workgroup each, and each workgroup writes its piece's normalised output and log-sum-exp as
 // fp32 partials (Op, Lp) for a merge pass (merge_kernel).  A piece (or half) that holds no
 // visible key for a row yields O = 0 and LSE = -inf there.
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART>
-__global__ void __launch_bounds__(NW * 64, 8 / NW)
+//
+// QB: 32-query blocks per wave.  With QB = 2 every K or V^T fragment read from LDS feeds two
+// MFMAs (one per block), which halves the LDS traffic per MFMA; a wave then needs about 400
+// registers, so each SIMD runs one wave (4-wave workgroups of 256 query rows, one per CU).
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART, int QB>
+__global__ void __launch_bounds__(NW * 64, 8 / (NW * QB))
 fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
            const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
            int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake, int n_part,
            float* __restrict__ Op, float* __restrict__ Lp) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
+  static_assert(NW * QB == 4 || NW * QB == 8, "one or two workgroups per CU");
   constexpr int GW = NW / SPLIT;            // waves per group
-  constexpr int BR = GW * 32, BC = kFwdBC;  // query rows per workgroup (32 per wave), keys per tile
+  constexpr int RW = 32 * QB;               // query rows per wave
+  constexpr int BR = GW * RW, BC = kFwdBC;  // query rows per workgroup, keys per tile
   constexpr int KST = HD / 16;              // k-steps of S^T over the head dim
   constexpr int DB = HD / 32;               // 32-row blocks of O^T
   constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
   constexpr int TI = TILE / 1024 / GW;      // 1 KB direct loads per wave per tile
   static_assert(TI * 1024 * GW == TILE, "tile must split into 1 KB loads over the waves");
 
-  // K/V tiles are loaded DIST steps ahead into NB = DIST + 1 buffers each.  One 8-wave
-  // workgroup per CU has LDS to spare for two steps of lead; two 4-wave workgroups share a
-  // CU and keep one, and so do the two groups of a split workgroup.
-  constexpr int DIST = (NW == 8 && SPLIT == 1) ? 2 : 1, NB = DIST + 1;
+  // K/V tiles are loaded DIST steps ahead into NB = DIST + 1 buffers each.  One workgroup per
+  // CU has LDS to spare for two steps of lead; two workgroups per CU keep one, and so do the
+  // two groups of a split workgroup.
+  constexpr int DIST = (NW * QB == 8 && SPLIT == 1) ? 2 : 1, NB = DIST + 1;
   // The running max is not tracked per tile.  Probabilities are formed against the reference
   // max, and the row sum, computed anyway, bounds every one of them: while a lane's share of
   // the tile's sum stays <= 2^7, no probability exceeds 2^8 and nothing needs to be rescaled.
@@ -86,6 +145,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // its K tile, still resident in one more K buffer, and the reference moves to their max.
   // This takes the 16 v_max3 and the cross-lane reduction per tile off the VALU.
   constexpr int NBK = NB + 1;
+  // 64-row waves: O accumulators and Q fragments in AGPRs (mfma_av, mfma_va).
+  constexpr bool AGPR = QB == 2;
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * (NBK + NB) * TILE];  // per group: K[NBK], V[NB]
 
   const int tid = threadIdx.x;
@@ -112,15 +173,17 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* const Kh = K + ((size_t)b * Hkv + hkv) * N * HD;
   const uint16_t* const Vh = V + ((size_t)b * Hkv + hkv) * N * HD;
 
-  const int qw0 = qt * BR + wv * 32;  // first query row of this wave
-  const int qi = qw0 + c;             // the query row this lane's column belongs to
+  const int qw0 = qt * BR + wv * RW;  // first query row of this wave
+  int qi[QB];                         // the query row of this lane's column in each block
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) qi[qb] = qw0 + qb * 32 + c;
 
   // K/V tiles the workgroup streams, and the prefix of them this wave computes on (causal
   // waves stop at their own diagonal; waves wholly past the last row compute nothing).
   int T = (N + BC - 1) / BC;
   if (CAUSAL) T = (min(N, (qt + 1) * BR) - 1) / BC + 1;
   int Tw = T;
-  if (CAUSAL) Tw = (min(N, qw0 + 32) - 1) / BC + 1;
+  if (CAUSAL) Tw = (min(N, qw0 + RW) - 1) / BC + 1;
   if (qw0 >= N) Tw = 0;
   // This group's tiles [t0, t0 + Tg) (group 0 takes the larger half), the steps every wave
   // takes (the larger group's tile count + 1, one barrier each), and the number of the
@@ -148,49 +211,66 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int r = 0; r < TI; ++r)
       dma_to_lds<16>(res, doff[r], (uint32_t)(t0 + t) * (BC * HD * 2), dst + (wv * TI + r) * 1024);
   };
-  if (0 < Tg) issue(rK, 0, sK);
-  if constexpr (DIST == 2) {
-    if (1 < Tg) issue(rK, 1, sK + TILE);
-    issue(rV, 0, sV);
-  }
-
-  // Q fragments: B operand of S^T = K Q^T (slot j of k-step kk = Q[qi][kk*16 + g*8 + j]).
-  u32x4 qf[KST];
+  auto issue_first = [&]() FA_INL {
+    if (0 < Tg) issue(rK, 0, sK);
+    if constexpr (DIST == 2) {
+      if (1 < Tg) issue(rK, 1, sK + TILE);
+      issue(rV, 0, sV);
+    }
+  };
+  // Q fragments: B operand of S^T = K Q^T (slot j of block qb, k-step kk = Q[qi[qb]][kk*16 + g*8 + j]).
+  // Fragments bound for AGPRs are moved there as soon as they land, so their loads go first
+  // (loads retire in order).
+  if constexpr (!AGPR) issue_first();
+  u32x4 qf[QB][KST];
 #pragma unroll
-  for (int kk = 0; kk < KST; ++kk) qf[kk] = ld16_if(Qh + (size_t)qi * HD + kk * 16 + g * 8, qi < N);
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      qf[qb][kk] = ld16_if(Qh + (size_t)qi[qb] * HD + kk * 16 + g * 8, qi[qb] < N);
+  if constexpr (AGPR) issue_first();
 
   // Per-lane LDS offsets.  K rows are read in the permuted order, so register i of an S^T
   // block is key (i/8)*16 + g*8 + i%8; one offset per k-step parity.
   const uint32_t koff[2] = {sl_off<BC>(perm_rows(c), g * 8), sl_off<BC>(perm_rows(c), 16 + g * 8)};
   const TrLane trl = tr_lane(lane);
 
-  f32x16 acc[DB];
+  f32x16 acc[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY;  // running (reference) max of raw scores for query qi
-  float l_run = 0.f;        // this lane's share of the running sum of 2^((s - m) * c2)
-  f32x16 p[2];              // probabilities of the previous tile, waiting for P V
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
+  if constexpr (AGPR) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) asm volatile("" : "+a"(qf[qb][kk]));  // Q moves to AGPRs once
+    reg_fence(qf, true, true);
+  }
+  float m_run[QB];  // running (reference) max of raw scores for query qi[qb]
+  float l_run[QB];  // this lane's share of the running sum of 2^((s - m) * c2)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = -INFINITY, l_run[qb] = 0.f;
+  f32x16 p[2][QB];  // probabilities of the previous tile (key block, query block), waiting for P V
 
   // ---- the pieces of one pipeline step; step j computes S_j and its softmax while the
   //      MFMAs of P_{j-1} V_{j-1} run, so the exp2 work hides under matrix work.  Each MFMA
-  //      step is fenced together with the LDS read of the operand RD steps ahead and a fixed
-  //      share of the VALU work, so the two pipes stay interleaved.
+  //      is fenced together with a fixed share of the VALU work (and, once per fragment, the
+  //      LDS read of the operand RD fragments ahead), so the two pipes stay interleaved.
   constexpr int RD = 4;
-  // K fragment of S-step i (i = kb*KST + kk): key rows kb*32.., head-dim k-step kk.  The
-  // first 32-key block is finished half way through, so its row max can start under the
-  // MFMAs of the second block.
+  // K fragment i (i = kb*KST + kk): key rows kb*32.., head-dim k-step kk.
   auto kfrag = [&](const char* tK, int i) FA_INL {
     const int kk = i % KST, kb = i / KST;
     return lds_ld128(tK + sl_off<BC>(kb * 32, (kk >> 1) * 32) + koff[kk & 1]);
   };
-  // V^T fragment of PV-step i (i = db*4 + kb*2 + t2).
+  // V^T fragment i (i = db*4 + kb*2 + t2).
   auto vfrag = [&](const char* tV, int i) FA_INL {
     const int db = i >> 2, kb = (i >> 1) & 1, t2 = i & 1;
     return lds_tr8(tV + sl_off<BC>(kb * 32 + t2 * 16, db * 32), trl);
   };
-  // S^T_j = K_j Q^T (register i of block kb holds key j*BC + kb*32 + (i/8)*16 + g*8 + i%8),
-  // with valu(i) run under S-step i.
-  auto scores = [&](const char* __restrict__ tK, f32x16 (&s)[2], auto&& valu) FA_INL {
+  // S^T_j = K_j Q^T (register i of block (kb, qb) holds key j*BC + kb*32 + (i/8)*16 + g*8 + i%8
+  // against query qi[qb]), with valu(i * QB + qb) run under the MFMA of fragment i, block qb.
+  auto scores = [&](const char* __restrict__ tK, f32x16 (&s)[2][QB], auto&& valu) FA_INL {
     constexpr int NS = 2 * KST;
     u32x4 ring[RD + 1];
 #pragma unroll
@@ -202,15 +282,30 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int i = 0; i < NS; ++i) {
       if (i + RD < NS) ring[(i + RD) % (RD + 1)] = kfrag(tK, i + RD);
       __builtin_amdgcn_sched_barrier(0);
-      s[i / KST] = TR::mfma(ring[i % (RD + 1)], qf[i % KST], s[i / KST]);
-      valu(i);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (!AGPR)
+          s[i / KST][qb] = TR::mfma(ring[i % (RD + 1)], qf[qb][i % KST], s[i / KST][qb]);
+        else if (i % KST == 0)  // (the loops are unrolled: one call remains per MFMA)
+          mfma_va0<TR, kNopNone>(s[i / KST][qb], ring[i % (RD + 1)], qf[qb][i % KST]);
+        else if (i == NS - 1 && qb == QB - 1)
+          mfma_va<TR, kNopAfter>(s[i / KST][qb], ring[i % (RD + 1)], qf[qb][i % KST]);
+        else
+          mfma_va<TR, kNopNone>(s[i / KST][qb], ring[i % (RD + 1)], qf[qb][i % KST]);
+        valu(i * QB + qb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    if constexpr (AGPR) reg_fence(s, false, false);
   };
   // O^T += V^T P^T (A = V^T: rows d, k = keys, read transposed from the V tile), with
-  // valu(i) run under PV-step i.
-  auto pv = [&](const char* __restrict__ tV, const u32x4 (&pb)[2][2], auto&& valu) FA_INL {
+  // valu(i * QB + qb) run under the MFMA of fragment i, block qb.
+  auto pv = [&](const char* __restrict__ tV, u32x4 (&pb)[2][2][QB], auto&& valu) FA_INL {
     constexpr int NS = DB * 4;
+    if constexpr (AGPR) {
+      reg_fence(acc, true, false);
+      reg_fence(reinterpret_cast<u32x4(&)[4][QB]>(pb), false, false);
+    }
     u32x4 ring[RD + 1];
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
@@ -221,70 +316,138 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int i = 0; i < NS; ++i) {
       if (i + RD < NS) ring[(i + RD) % (RD + 1)] = vfrag(tV, i + RD);
       __builtin_amdgcn_sched_barrier(0);
-      acc[i >> 2] = TR::mfma(ring[i % (RD + 1)], pb[(i >> 1) & 1][i & 1], acc[i >> 2]);
-      valu(i);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (AGPR) {  // (the loops are unrolled: one call remains per MFMA)
+          f32x16& o = acc[qb][i >> 2];
+          const u32x4 a = ring[i % (RD + 1)], b = pb[(i >> 1) & 1][i & 1][qb];
+          if (i == 0 && qb == 0)
+            mfma_av<TR, kNopBefore>(o, a, b);
+          else if (i == NS - 1 && qb == QB - 1)
+            mfma_av<TR, kNopAfter>(o, a, b);
+          else
+            mfma_av<TR, kNopNone>(o, a, b);
+        }
+        else
+          acc[qb][i >> 2] = TR::mfma(ring[i % (RD + 1)], pb[(i >> 1) & 1][i & 1][qb], acc[qb][i >> 2]);
+        valu(i * QB + qb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   // Masks, needed only on a wave's last tile (the ragged end of the keys, or the tile that
   // holds this wave's diagonal): masked scores become -inf, so exp2 (with c2 > 0) makes
   // exact zeros.
-  auto mask = [&](int j, f32x16 (&s)[2]) FA_INL {
+  auto mask = [&](int j, f32x16 (&s)[2][QB]) FA_INL {
+    const int kv0 = (t0 + j) * BC;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          if (key >= N || (CAUSAL && key > qi[qb])) s[kb][qb][i] = -INFINITY;
+        }
+  };
+  // One query block of S^T (the rare path): register i of r[kb][0] as in `scores`.
+  auto scores_q = [&](const char* __restrict__ tK, int qb, f32x16 (&r)[2][1]) FA_INL {
+#pragma unroll
+    for (int i = 0; i < 2 * KST; ++i) {
+      const u32x4 a = kfrag(tK, i);
+      if constexpr (!AGPR)
+        r[i / KST][0] = TR::mfma(a, qf[qb][i % KST], r[i / KST][0]);
+      else if (i % KST == 0)
+        mfma_va0<TR, kNopNone>(r[i / KST][0], a, qf[qb][i % KST]);
+      else if (i == 2 * KST - 1)
+        mfma_va<TR, kNopAfter>(r[i / KST][0], a, qf[qb][i % KST]);
+      else
+        mfma_va<TR, kNopNone>(r[i / KST][0], a, qf[qb][i % KST]);
+    }
+    if constexpr (AGPR) reg_fence(r, false, false);  // no read of r moves above the last MFMA
+  };
+  auto mask_q = [&](int j, int qb, f32x16 (&r)[2][1]) FA_INL {
     const int kv0 = (t0 + j) * BC;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kv0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-        if (key >= N || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
+        if (key >= N || (CAUSAL && key > qi[qb])) r[kb][0][i] = -INFINITY;
       }
   };
   // Online softmax in raw-score units (c2 = scale * log2(e) > 0), as units u of work (see
-  // sm_step).  The full set (maxima, reduction, exp2) runs on a wave's first tile, where the
+  // kSmUnits).  The full set (maxima, reduction, exp2) runs on a wave's first tile, where the
   // reference max is set (kRescaleLog2 only decides whether it moves there; it always does
   // from -inf); the steady steps run the exp2 units alone (see check / redo).  When the
   // reference moves, O is scaled by alpha before the next P V.
   bool need = false;  // uniform: O must be scaled by alpha before the next P V
-  float alpha = 1.f;
-  float mx0 = 0.f, mx1 = 0.f, mb = 0.f;
-  auto softmax_unit = [&](f32x16 (&s)[2], int u) FA_INL {
-    if (u < kSmMax) {  // two running maxima, one per 32-key block, one v_max3 each step
-      const int kb = u >> 3, e = (u & 7) * 2;
-      float& m = kb ? mx1 : mx0;
-      if ((u & 7) == 0)
-        m = fmaxf(s[kb][0], s[kb][1]);
+  float alpha[QB], mx0[QB], mx1[QB], mb[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) alpha[qb] = 1.f, mx0[qb] = mx1[qb] = mb[qb] = 0.f;
+  auto softmax_unit = [&](f32x16 (&s)[2][QB], int u) FA_INL {
+    const int qb = u % QB, v = u / QB;
+    if (v < kSmMax) {  // two running maxima, one per 32-key block, one v_max3 each step
+      const int kb = v >> 3, e = (v & 7) * 2;
+      float& m = kb ? mx1[qb] : mx0[qb];
+      if ((v & 7) == 0)
+        m = fmaxf(s[kb][qb][0], s[kb][qb][1]);
       else
-        m = fmaxf(fmaxf(m, s[kb][e]), s[kb][e + 1]);
-    } else if (u == kSmRed) {
-      const float mx = pair_max(fmaxf(mx0, mx1));
-      const float m_new = fmaxf(m_run, mx);  // finite: key 0 is visible to every row
-      need = __builtin_amdgcn_ballot_w64((m_new - m_run) * c2 > kRescaleLog2) != 0;
-      alpha = need ? fast_exp2((m_run - m_new) * c2) : 1.f;
-      m_run = need ? m_new : m_run;
-      l_run *= alpha;
-      mb = m_run * c2;
+        m = fmaxf(fmaxf(m, s[kb][qb][e]), s[kb][qb][e + 1]);
+    } else if (v == kSmRed) {
+      const float mx = pair_max(fmaxf(mx0[qb], mx1[qb]));
+      const float m_new = fmaxf(m_run[qb], mx);  // finite: key 0 is visible to every row
+      const bool nq = __builtin_amdgcn_ballot_w64((m_new - m_run[qb]) * c2 > kRescaleLog2) != 0;
+      alpha[qb] = nq ? fast_exp2((m_run[qb] - m_new) * c2) : 1.f;
+      m_run[qb] = nq ? m_new : m_run[qb];
+      l_run[qb] *= alpha[qb];
+      mb[qb] = m_run[qb] * c2;
+      need = need || nq;
     } else {
-      const int e = u - kSmExp0, kb = e >> 4, i = e & 15;
-      s[kb][i] = fast_exp2(fmaf(s[kb][i], c2, -mb));
+      const int e = v - kSmExp0, kb = e >> 4, i = e & 15;
+      s[kb][qb][i] = fast_exp2(fmaf(s[kb][qb][i], c2, -mb[qb]));
     }
   };
-  auto softmax_all = [&](f32x16 (&s)[2]) FA_INL {
+  auto softmax_all = [&](f32x16 (&s)[2][QB]) FA_INL {
 #pragma unroll
-    for (int u = 0; u < kSmUnits; ++u) softmax_unit(s, u);
+    for (int u = 0; u < kSmUnits * QB; ++u) softmax_unit(s, u);
   };
-  // P^T operands (slot j of (kb, t2) = P for key kb*32 + t2*16 + g*8 + j) and the row sum,
-  // as 16 units: unit i packs pair i%4 of operand (i/8, (i/4)%2) and adds its two values.
-  // fp16 sums the rounded pair in one dot2 (relative rounding 2^-12, far inside the LSE
-  // tolerance even for a row with one visible key); bf16 rounding (2^-9) is not, so bf16
-  // sums the fp32 values.
-  float rs = 0.f;
-  auto pack_unit = [&](u32x4 (&pb)[2][2], int i) FA_INL {
-    const int kb = i >> 3, t2 = (i >> 2) & 1, pr = i & 3, e = t2 * 8 + pr * 2;
-    pb[kb][t2][pr] = TR::pack(p[kb][e], p[kb][e + 1]);
+  // P^T operands (slot j of (kb, t2, qb) = P for key kb*32 + t2*16 + g*8 + j) and the row sums,
+  // as 16 units per query block: unit v of block qb packs pair v%4 of operand (v/8, (v/4)%2)
+  // and adds its two values.  fp16 sums the rounded pair in one dot2 (relative rounding 2^-12,
+  // far inside the LSE tolerance even for a row with one visible key); bf16 rounding (2^-9) is
+  // not, so bf16 sums the fp32 values.
+  float rs[QB];
+  auto pack_unit = [&](u32x4 (&pb)[2][2][QB], int u) FA_INL {
+    const int qb = u % QB, v = u / QB;
+    const int kb = v >> 3, t2 = (v >> 2) & 1, pr = v & 3, e = t2 * 8 + pr * 2;
+    pb[kb][t2][qb][pr] = TR::pack(p[kb][qb][e], p[kb][qb][e + 1]);
     if constexpr (std::is_same<TR, F16>::value)
-      rs = TR::add_pair(pb[kb][t2][pr], rs);
+      rs[qb] = TR::add_pair(pb[kb][t2][qb][pr], rs[qb]);
     else
-      rs += p[kb][e] + p[kb][e + 1];
+      rs[qb] += p[kb][qb][e] + p[kb][qb][e + 1];
+  };
+  auto zero_rs = [&]() FA_INL {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) rs[qb] = -0.f;  // (x + -0 = x folds away)
+  };
+  // O *= alpha (rare).  Accumulators in AGPRs pass through VGPRs one block at a time, with
+  // each move written out so that the accumulators are never allocated to VGPRs.
+  auto scale_acc = [&]() FA_INL {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if constexpr (AGPR) {
+          f32x16 t;
+          asm volatile("" : "=v"(t) : "0"(acc[qb][db]));
+          t *= alpha[qb];
+          asm volatile("" : "=a"(acc[qb][db]) : "0"(t));
+        } else {
+          acc[qb][db] *= alpha[qb];
+        }
+      }
+    if constexpr (AGPR) reg_fence(acc, true, true);
   };
 
   // Pipeline step j (0 <= j <= T), one per K/V tile plus a drain: waits for K_j and V_{j-1},
@@ -294,38 +457,64 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   enum Kind { kFirst, kFirstMasked, kSteady, kSteadyMasked, kDrain, kIdle };
   // The rare path: P_{jp} (the previous tile, its K tile in tKp) is recomputed with
   // the reference moved to the tile's max; l is rescaled here and O (flagged by `need`) just
-  // before P_{jp} V_{jp} is added.
-  auto redo = [&](const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2]) FA_INL {
-    p[0] = f32x16{};
-    p[1] = f32x16{};
-    scores(tKp, p, [](int) FA_INL {});
-    mask(jp, p);  // a no-op unless jp is the wave's last tile
-    float mx = -INFINITY;
+  // before P_{jp} V_{jp} is added.  One query block at a time, which keeps the path's registers
+  // within those of the steady path.  Only the drain step's tile can need masks (`masked`).
+  auto redo = [&](auto masked, const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2][QB]) FA_INL {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 r[2][1];
+      r[0][0] = f32x16{};
+      r[1][0] = f32x16{};
+      scores_q(tKp, qb, r);
+      if constexpr (decltype(masked)::value) mask_q(jp, qb, r);
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, p[kb][i]);
-    const float m_new = fmaxf(m_run, pair_max(mx));
-    alpha = fast_exp2((m_run - m_new) * c2);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, r[kb][0][i]);
+      const float m_new = fmaxf(m_run[qb], pair_max(mx));
+      alpha[qb] = fast_exp2((m_run[qb] - m_new) * c2);
+      l_run[qb] *= alpha[qb];
+      m_run[qb] = m_new;
+      mb[qb] = m_new * c2;
+      rs[qb] = -0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const int e = t2 * 8 + pr * 2;
+            const float x0 = fast_exp2(fmaf(r[kb][0][e], c2, -mb[qb]));
+            const float x1 = fast_exp2(fmaf(r[kb][0][e + 1], c2, -mb[qb]));
+            pb[kb][t2][qb][pr] = TR::pack(x0, x1);
+            if constexpr (std::is_same<TR, F16>::value)
+              rs[qb] = TR::add_pair(pb[kb][t2][qb][pr], rs[qb]);
+            else
+              rs[qb] += x0 + x1;
+          }
+    }
     need = true;
-    l_run *= alpha;
-    m_run = m_new;
-    mb = m_run * c2;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[kb][i] = fast_exp2(fmaf(p[kb][i], c2, -mb));
-    rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pack_unit(pb, i);
   };
-  auto check = [&](const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2]) FA_INL {
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(rs <= 0x1p7f)) != 0, 0)) redo(tKp, jp, pb);
-    if (need) {
+  auto check = [&](auto masked, const char* __restrict__ tKp, int jp, u32x4 (&pb)[2][2][QB]) FA_INL {
+    bool over = false;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    for (int qb = 0; qb < QB; ++qb) over = over || !(rs[qb] <= 0x1p7f);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) redo(masked, tKp, jp, pb);
+    if (need) {
+      scale_acc();
       need = false;
     }
+  };
+  auto add_rs = [&]() FA_INL {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+  };
+  auto keep_p = [&](const f32x16 (&s)[2][QB]) FA_INL {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) p[kb][qb] = s[kb][qb];
   };
 
   auto step = [&](auto kind_tag, const int j, char* __restrict__ nK, char* __restrict__ nV,
@@ -346,8 +535,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     lds_barrier();  // ... and everyone's; everyone is also done with step j-1's buffers
     if (need) {       // the max moved in the previous step: rescale O (rare)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      scale_acc();
       need = false;
     }
     if (j + DIST < Tg) issue(rK, j + DIST, nK);
@@ -355,41 +543,51 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (KIND == kSteady || KIND == kSteadyMasked) {
       // [S_j MFMAs | pack P_{j-1}]  [P_{j-1} V_{j-1} MFMAs | softmax of S_j]
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      u32x4 pb[2][2];
-      rs = 0.f;
+      f32x16 s[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+      u32x4 pb[2][2][QB];
+      zero_rs();
       // The steady steps run only the exp2 units of the softmax (FIRST = kSmExp0); the masks
       // of a masked tile come after its S MFMAs.
-      constexpr int NS = 2 * KST, FIRST = kSmExp0;
+      // The units are spread evenly over the MFMAs of each phase.
+      constexpr int NSM = 2 * KST * QB, NPV = DB * 4 * QB, FIRST = kSmExp0, NP = 16 * QB;
       scores(tK, s, [&](int i) FA_INL {
 #pragma unroll
-        for (int u = i * 16 / NS; u < (i + 1) * 16 / NS; ++u) pack_unit(pb, u);
+        for (int u = 0; u < NP; ++u)
+          if (u * NSM / NP == i) pack_unit(pb, u);
       });
-      check(pK, j - 1, pb);
-      l_run += rs;
+      check(std::false_type{}, pK, j - 1, pb);
+      add_rs();
       if constexpr (KIND == kSteadyMasked) mask(j, s);
+      // (the steady steps run exp2 units only, all of equal weight)
+      constexpr int NX = (kSmUnits - FIRST) * QB;
       pv(tV, pb, [&](int i) FA_INL {
 #pragma unroll
-        for (int u = FIRST; u < kSmUnits; ++u)
-          if (sm_step(u, DB * 4, FIRST) == i) softmax_unit(s, u);
+        for (int x = 0; x < NX; ++x)
+          if (x * NPV / NX == i) softmax_unit(s, FIRST * QB + x);
       });
-      p[0] = s[0];
-      p[1] = s[1];
+      keep_p(s);
     } else if constexpr (KIND == kFirst || KIND == kFirstMasked) {
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      f32x16 s[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
       scores(tK, s, [](int) FA_INL {});
       if constexpr (KIND == kFirstMasked) mask(j, s);
       softmax_all(s);
       need = false;  // O is still zero
-      p[0] = s[0];
-      p[1] = s[1];
+      keep_p(s);
     } else if constexpr (KIND == kDrain) {
-      u32x4 pb[2][2];
-      rs = 0.f;
+      u32x4 pb[2][2][QB];
+      zero_rs();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pack_unit(pb, i);
-      check(pK, j - 1, pb);
-      l_run += rs;
+      for (int u = 0; u < 16 * QB; ++u) pack_unit(pb, u);
+      check(std::true_type{}, pK, j - 1, pb);
+      add_rs();
       pv(tV, pb, [](int) FA_INL {});
     }
   };
@@ -435,78 +633,82 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     run(KDrain{}, Twg);
     for (int j = Twg + 1; j <= half; ++j) run(KIdle{}, j);
   }
-  if (need) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-  }
+  if constexpr (AGPR) reg_fence(acc, true, false);
+  if (need) scale_acc();
 
   // ---- split workgroups: group 1 hands its (O, running max, running sum) to the group-0 wave
   // that owns the same rows, through LDS (the K/V buffers are free once every wave has passed
   // the barrier).  Both halves are rescaled to the larger max: exp2 of (m_h - m) * c2, which is
   // 0 for a half that saw no key (m_h = -inf).
   if constexpr (SPLIT == 2) {
-    constexpr int XW = 16 * DB + 2;  // floats per lane: O, max, sum
+    constexpr int XB = 16 * DB + 2, XW = QB * XB;  // floats per lane and block: O, max, sum
     static_assert(GW * 64 * XW * 4 <= (int)sizeof(smem), "exchange must fit in the K/V buffers");
     float* const xs = reinterpret_cast<float*>(smem) + wv * (64 * XW) + lane;
     lds_barrier();
     if (grp == 1) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xs[(db * 16 + i) * 64] = acc[db][i];
-      xs[(16 * DB) * 64] = m_run;
-      xs[(16 * DB + 1) * 64] = l_run;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xs[(qb * XB + db * 16 + i) * 64] = acc[qb][db][i];
+        xs[(qb * XB + 16 * DB) * 64] = m_run[qb];
+        xs[(qb * XB + 16 * DB + 1) * 64] = l_run[qb];
+      }
     }
     lds_barrier();
     if (grp == 1) return;
-    const float m1 = xs[(16 * DB) * 64], l1 = xs[(16 * DB + 1) * 64];
-    const float m = fmaxf(m_run, m1);
-    // (equal maxima take weight 1, which also keeps two empty halves, m = -inf, NaN-free)
-    const float a0 = m_run == m ? 1.f : fast_exp2((m_run - m) * c2);
-    const float a1 = m1 == m ? 1.f : fast_exp2((m1 - m) * c2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m1 = xs[(qb * XB + 16 * DB) * 64], l1 = xs[(qb * XB + 16 * DB + 1) * 64];
+      const float m = fmaxf(m_run[qb], m1);
+      // (equal maxima take weight 1, which also keeps two empty halves, m = -inf, NaN-free)
+      const float a0 = m_run[qb] == m ? 1.f : fast_exp2((m_run[qb] - m) * c2);
+      const float a1 = m1 == m ? 1.f : fast_exp2((m1 - m) * c2);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] = acc[db][i] * a0 + xs[(db * 16 + i) * 64] * a1;
-    l_run = l_run * a0 + l1 * a1;
-    m_run = m;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[qb][db][i] = acc[qb][db][i] * a0 + xs[(qb * XB + db * 16 + i) * 64] * a1;
+      l_run[qb] = l_run[qb] * a0 + l1 * a1;
+      m_run[qb] = m;
+    }
   }
 
   // ---- epilogue: normalise, write O (input dtype, RNE) and LSE (natural log, fp32)
-  const float l_tot = pair_sum(l_run);
-  if constexpr (PART) {
-    // fp32 partials of piece `part`; a row with no visible key in the piece: O = 0, LSE = -inf
-    if (qi < N) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = pair_sum(l_run[qb]);
+    if (qi[qb] >= N) continue;
+    if constexpr (PART) {
+      // fp32 partials of piece `part`; a row with no visible key in the piece: O = 0, LSE = -inf
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       const size_t rows = (size_t)(gridDim.x / (n_part * n_qt)) * N;  // B * Hq * N
-      const size_t row = (size_t)part * rows + (size_t)bh * N + qi;
+      const size_t row = (size_t)part * rows + (size_t)bh * N + qi[qb];
       float* const orow = Op + row * HD;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d = db * 32 + i4 * 8 + g * 4;
-          const f32x4 w = {acc[db][i4 * 4 + 0] * inv, acc[db][i4 * 4 + 1] * inv, acc[db][i4 * 4 + 2] * inv,
-                           acc[db][i4 * 4 + 3] * inv};
+          const f32x4 w = {acc[qb][db][i4 * 4 + 0] * inv, acc[qb][db][i4 * 4 + 1] * inv,
+                           acc[qb][db][i4 * 4 + 2] * inv, acc[qb][db][i4 * 4 + 3] * inv};
           *reinterpret_cast<f32x4*>(orow + d) = w;
         }
-      if (g == 0) Lp[row] = l_tot > 0.f ? m_run * scale + __logf(l_tot) : -INFINITY;
+      if (g == 0) Lp[row] = l_tot > 0.f ? m_run[qb] * scale + __logf(l_tot) : -INFINITY;
+    } else {
+      const float inv = 1.f / l_tot;
+      uint16_t* const orow = O + (size_t)bh * N * HD + (size_t)qi[qb] * HD;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = db * 32 + i4 * 8 + g * 4;
+          const u32x2 w = {TR::pack(acc[qb][db][i4 * 4 + 0] * inv, acc[qb][db][i4 * 4 + 1] * inv),
+                           TR::pack(acc[qb][db][i4 * 4 + 2] * inv, acc[qb][db][i4 * 4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d) = w;
+        }
+      if (g == 0) LSE[(size_t)bh * N + qi[qb]] = m_run[qb] * scale + __logf(l_tot);
     }
-    return;
-  }
-  const float inv = 1.f / l_tot;
-  if (qi < N) {
-    uint16_t* const orow = O + (size_t)bh * N * HD + (size_t)qi * HD;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = db * 32 + i4 * 8 + g * 4;
-        const u32x2 w = {TR::pack(acc[db][i4 * 4 + 0] * inv, acc[db][i4 * 4 + 1] * inv),
-                         TR::pack(acc[db][i4 * 4 + 2] * inv, acc[db][i4 * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-    if (g == 0) LSE[(size_t)bh * N + qi] = m_run * scale + __logf(l_tot);
   }
 }
 
@@ -516,31 +718,33 @@ inline bool fwd_split_kv(const FwdArgs& a) {
   return a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512;
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false, int QB = 1>
 hipError_t launch_fwd_nw(const FwdArgs& a) {
-  constexpr int BR = NW / SPLIT * 32;
+  constexpr int BR = NW / SPLIT * 32 * QB;
   const int n_qt = (int)((a.N + BR - 1) / BR);
   const int n_part = PART ? a.n_part : 1;
   const long long blocks = a.B * a.Hq * (long long)n_qt * n_part;
   // c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
   // becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
   const float c2 = a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f;
-  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW, SPLIT, PART>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW, SPLIT, PART, QB>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale, (int)grid_fits(blocks, 8 / NW), n_part,
+                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale, (int)grid_fits(blocks, 8 / (NW * QB)), n_part,
                      a.o_part, a.lse_part);
   return hipGetLastError();
 }
 
-// 256-query workgroups (8 waves, one workgroup per CU) halve the K/V traffic from L2 per
-// query.  Smaller grids use 128-query tiles: as 8-wave workgroups that split the key range
-// over two wave groups (one per CU), which keeps two waves on every SIMD and evens out causal
-// work, or as 4-wave workgroups (two per CU).
+// 256-query workgroups (one per CU) halve the K/V traffic from L2 per query; they run as 4
+// waves of 64 query rows, which also halves the LDS reads per MFMA (measured: 1.4-2% faster
+// than 8 waves of 32 rows at N >= 8192, the same at N = 4096; the forward is power-bound).
+// Smaller grids use 128-query tiles: as 8-wave workgroups that split the key range over two
+// wave groups (one per CU), which keeps two waves on every SIMD and evens out causal work, or
+// as 4-wave workgroups (two per CU).
 template <typename TR, int HD, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a) {
   const long long big = a.B * a.Hq * ((a.N + 255) / 256);
-  if (big >= 512) return launch_fwd_nw<TR, HD, CAUSAL, 8, 1>(a);
+  if (big >= 512) return launch_fwd_nw<TR, HD, CAUSAL, 4, 1, false, 2>(a);
   if (fwd_split_kv(a)) return launch_fwd_nw<TR, HD, CAUSAL, 8, 2>(a);
   return launch_fwd_nw<TR, HD, CAUSAL, 4, 1>(a);
 }
