@@ -159,50 +159,68 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // K and V rows of this lane's key as B operands: slot j of k-step kk = K[key][kk*16 + g*8 + j]
   // (zero past the end: those keys' dK/dV are never stored).
-  u32x4 kf[KST], vf[KST];
+  // They are only ever MFMA B operands and stay in AGPRs, as do the dK/dV accumulators, which
+  // only MFMAs touch until the epilogue (written-out MFMAs, see fa_device.h); S and dP land in
+  // VGPRs for the VALU.
+  u32x4 kv[2][KST];  // [0] K, [1] V
 #pragma unroll
   for (int kk = 0; kk < KST; ++kk) {
-    kf[kk] = ld16_if(K + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
-    vf[kk] = ld16_if(V + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
+    kv[0][kk] = ld16_if(K + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
+    kv[1][kk] = ld16_if(V + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
   }
+  reg_fence(kv, true, true);
 
   // Per-lane LDS offsets: Q/dO rows in the permuted order, so register i of a unit's S/dP
   // block is query (i/8)*16 + g*8 + i%8; one offset per k-step parity.
   const uint32_t qoff[2] = {sl_off<BQ>(perm_rows(c), g * 8), sl_off<BQ>(perm_rows(c), 16 + g * 8)};
   const TrLane trl = tr_lane(lane);
 
-  f32x16 dKa[DB], dVa[DB];
+  f32x16 acc[2][DB];  // [0] dK, [1] dV
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    dKa[db] = f32x16{};
-    dVa[db] = f32x16{};
+    acc[0][db] = f32x16{};
+    acc[1][db] = f32x16{};
   }
 
   // ---- pipeline pieces.  A unit is (query tile qt, block qb): queries qt*BQ + qb*32 + 0..31,
-  //      held in the LDS slot `sl` of its tile.
-  // S = Q K^T and dP = dO V^T of a unit (16 MFMAs), with valu(i) under MFMA i.
-  auto sdp = [&](const char* sl, int qb, f32x16& s, f32x16& dp, auto&& valu) FA_INL {
-    const char* tQ = sl;
-    const char* tdO = sl + OFF_DO;
-    auto frag = [&](int i) FA_INL {  // i = kk*2 + (0: Q, 1: dO)
-      const int kk = i >> 1;
-      const uint32_t o = sl_off<BQ>(qb * 32, (kk >> 1) * 32) + qoff[kk & 1];
-      return lds_ld128(((i & 1) ? tdO : tQ) + o);
-    };
+  //      held in the LDS slot `sl` of its tile.  One wave runs per SIMD, so nothing else
+  //      covers the latency of a phase's first LDS reads: each phase's first RD operand
+  //      fragments, and a unit's per-query values, are read during the phase before.
+  // Operand fragment i of S = Q K^T / dP = dO V^T (i = kk*2 + (0: Q, 1: dO)) of block qb.
+  auto sdp_frag = [&](const char* sl, int qb, int i) FA_INL {
+    const int kk = i >> 1;
+    const uint32_t o = sl_off<BQ>(qb * 32, (kk >> 1) * 32) + qoff[kk & 1];
+    return lds_ld128(sl + ((i & 1) ? OFF_DO : 0) + o);
+  };
+  // Operand fragment i of dV += P^T dO / dK += dS^T Q (i = (db*2 + t2)*2 + (0: dO, 1: Q)),
+  // read transposed.
+  auto dvdk_frag = [&](const char* sl, int qb, int i) FA_INL {
+    const int db = i >> 2, t2 = (i >> 1) & 1;
+    const uint32_t o = sl_off<BQ>(qb * 32 + t2 * 16, db * 32);
+    return lds_tr8(sl + ((i & 1) ? 0 : OFF_DO) + o, trl);
+  };
+  // S and dP of a unit (16 MFMAs), with valu(i) under MFMA i.  Its first RD fragments come in
+  // `pre`; in the last RD steps, where none of its own remain to be read, it reads the next
+  // phase's first fragments (next(r), r < RD) into `post`.
+  auto sdp = [&](const char* sl, int qb, f32x16& s, f32x16& dp, const u32x4 (&pre)[RD], auto&& next,
+                 u32x4 (&post)[RD], auto&& valu) FA_INL {
+    constexpr int NS = 2 * KST;
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      ring[i] = frag(i);  // in use order, so each wait is partial
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int i = 0; i < RD; ++i) ring[i] = pre[i];
 #pragma unroll
-    for (int i = 0; i < 2 * KST; ++i) {
-      if (i + RD < 2 * KST) ring[(i + RD) % (RD + 1)] = frag(i + RD);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i & 1)
-        dp = TR::mfma(ring[i % (RD + 1)], vf[i >> 1], dp);
+    for (int i = 0; i < NS; ++i) {
+      if (i + RD < NS)
+        ring[(i + RD) % (RD + 1)] = sdp_frag(sl, qb, i + RD);
       else
-        s = TR::mfma(ring[i % (RD + 1)], kf[i >> 1], s);
+        post[i + RD - NS] = next(i + RD - NS);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i & 1)  // (the loops are unrolled: one call remains per MFMA)
+        mfma_va<TR, kNopNone>(dp, ring[i % (RD + 1)], kv[1][i >> 1]);
+      else if (i == 0)
+        mfma_va0<TR, kNopNone>(s, ring[i % (RD + 1)], kv[0][0]);
+      else
+        mfma_va<TR, kNopNone>(s, ring[i % (RD + 1)], kv[0][i >> 1]);
       valu(i);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -211,15 +229,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // query qb*32 + (i/8)*16 + g*8 + i%8, so four 16-byte reads give all sixteen in order.
   // LSE*log2(e) feeds P; -D (stored negated by the preprocess) is the accumulator input of the
   // dP MFMAs, which then produce dP - D directly.
-  struct RowVals {
-    f32x4 l[4];
-  };
   auto rowvals = [&](const char* sl, int qb) FA_INL {
-    RowVals r;
     const float* tL = reinterpret_cast<const float*>(sl + OFF_L);
+    f32x4 l[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) r.l[t] = *reinterpret_cast<const f32x4*>(tL + qb * 32 + (t >> 1) * 16 + g * 8 + (t & 1) * 4);
-    return r;
+    for (int t = 0; t < 4; ++t) l[t] = *reinterpret_cast<const f32x4*>(tL + qb * 32 + (t >> 1) * 16 + g * 8 + (t & 1) * 4);
+    return f32x16{l[0][0], l[0][1], l[0][2], l[0][3], l[1][0], l[1][1], l[1][2], l[1][3],
+                  l[2][0], l[2][1], l[2][2], l[2][3], l[3][0], l[3][1], l[3][2], l[3][3]};
   };
   auto neg_d = [&](const char* sl, int qb) FA_INL {
     const float* tD = reinterpret_cast<const float*>(sl + OFF_D);
@@ -235,10 +251,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // then P, then dS and the packing), so that consecutive MFMA steps can carry stages of
   // different units: with one wave per SIMD, a dependent chain inside one step would stall
   // the in-order issue.
-  auto pds_a = [&](f32x16& s, const RowVals& rv, int i) FA_INL {
-    const int t2 = i >> 3, j = i & 7;
-    s[i] = fmaf(s[i], c2, -rv.l[t2 * 2 + (j >> 2)][j & 3]);
-  };
+  auto pds_a = [&](f32x16& s, const f32x16& l2, int i) FA_INL { s[i] = fmaf(s[i], c2, -l2[i]); };
   auto pds_b = [&](f32x16& s, int i) FA_INL { s[i] = fast_exp2(s[i]); };
   auto pds_c = [&](f32x16& s, const f32x16& dp, u32x4 (&pa)[2], u32x4 (&dsa)[2], float (&pt)[2], float (&dt)[2],
                    int i) FA_INL {
@@ -261,119 +274,148 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       if (key > q) s[i] = -INFINITY;
     }
   };
-  // dV += P^T dO and dK += dS^T Q of a unit (16 MFMAs); B operands read transposed.
-  auto dvdk = [&](const char* sl, int qb, const u32x4 (&pa)[2], const u32x4 (&dsa)[2]) FA_INL {
-    const char* tQ = sl;
-    const char* tdO = sl + OFF_DO;
-    auto frag = [&](int i) FA_INL {  // i = (db*2 + t2)*2 + (0: dO, 1: Q)
-      const int db = i >> 2, t2 = (i >> 1) & 1;
-      const uint32_t o = sl_off<BQ>(qb * 32 + t2 * 16, db * 32);
-      return lds_tr8(((i & 1) ? tQ : tdO) + o, trl);
-    };
+  // dV += P^T dO and dK += dS^T Q of a unit (16 MFMAs).  Its first RD fragments come in `pre`;
+  // `ahead()` runs after the first MFMA (the reads for the next unit), and in the last RD steps
+  // it reads the next phase's first fragments (next(r)) into `post`, if HAS_POST.
+  // `rare` (the last unit, which runs outside the loop): the register allocator may move
+  // accumulator blocks there with v_accvgpr copies just before the MFMA that reads them, so
+  // every MFMA of that unit waits 2 first.  `tail`: the epilogue follows.
+  auto dvdk = [&](auto rare_tag, auto tail_tag, auto has_post_tag, const char* sl, int qb, const u32x4 (&pa)[2],
+                  const u32x4 (&dsa)[2], const u32x4 (&pre)[RD], auto&& ahead, auto&& next,
+                  u32x4 (&post)[RD]) FA_INL {
+    constexpr int NS = 4 * DB;
     u32x4 ring[RD + 1];
 #pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      ring[i] = frag(i);  // in use order, so each wait is partial
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int i = 0; i < RD; ++i) ring[i] = pre[i];
 #pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      if (i + RD < 4 * DB) ring[(i + RD) % (RD + 1)] = frag(i + RD);
+    for (int i = 0; i < NS; ++i) {
+      if (i + RD < NS)
+        ring[(i + RD) % (RD + 1)] = dvdk_frag(sl, qb, i + RD);
+      else if constexpr (decltype(has_post_tag)::value)
+        post[i + RD - NS] = next(i + RD - NS);
       __builtin_amdgcn_sched_barrier(0);
       const int db = i >> 2, t2 = (i >> 1) & 1;
-      if (i & 1)
-        dKa[db] = TR::mfma(dsa[t2], ring[i % (RD + 1)], dKa[db]);
+      const u32x4 a = (i & 1) ? dsa[t2] : pa[t2];
+      f32x16& o = acc[(i & 1) ? 0 : 1][db];
+      if (i == 0 || decltype(rare_tag)::value)  // (P and dS were packed by the VALU just before)
+        mfma_av<TR, kNopBefore>(o, a, ring[i % (RD + 1)]);
+      else if (decltype(tail_tag)::value && i == NS - 1)  // the epilogue reads the accumulators
+        mfma_av<TR, kNopAfter>(o, a, ring[i % (RD + 1)]);
       else
-        dVa[db] = TR::mfma(pa[t2], ring[i % (RD + 1)], dVa[db]);
+        mfma_av<TR, kNopNone>(o, a, ring[i % (RD + 1)]);
+      if (i == 0) ahead();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // One pipeline iteration for unit (qt, qb) held in slot `sl`: [S/dP of the next unit, held
-  // in `nsl` | P, dS of this unit] then [dV, dK of this unit].  (cs, cdp) hold this unit's
-  // S/dP, (ns, ndp) receive the next one's.
-  auto unit = [&](auto masked_tag, auto has_next_tag, int qt, int qb, const char* sl, const char* nsl,
-                  f32x16& cs, f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // Pipeline state carried from unit to unit: the LSE*log2(e) values of the current unit, -D
+  // of the next one (the dP accumulator input of its S/dP phase) and the first fragments of
+  // that phase.
+  f32x16 l2c, ndc;
+  u32x4 sdp_pre[RD];
+
+  // One pipeline iteration for unit u = (qt, qb) in slot `sl`: [S/dP of unit u+1 (slot `nsl`) |
+  // P, dS of unit u] then [dV, dK of unit u | reads for units u+1 and u+2 (slot `n2sl`)].
+  // (cs, cdp) hold u's S/dP, (ns, ndp) receive u+1's.  HAS_NEXT2: unit u+2 exists.
+  auto unit = [&](bool masked, auto has_next_tag, auto has_next2_tag, int qt, int qb, const char* sl,
+                  const char* nsl, const char* n2sl, f32x16& cs, f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    const RowVals rv = rowvals(sl, qb);
-    if constexpr (MASKED) mask(cs, qt * BQ + qb * 32);
-    u32x4 pa[2], dsa[2];
+    constexpr bool HAS_NEXT2 = decltype(has_next2_tag)::value;
+    const f32x16 l2 = l2c;
+    if (CAUSAL && masked) mask(cs, qt * BQ + qb * 32);  // (uniform)
+    u32x4 pa[2], dsa[2], dvdk_pre[RD];
     float pt[2], dt[2];
     if constexpr (HAS_NEXT) {
-      ns = f32x16{};
-      ndp = neg_d(nsl, qb ^ 1);
+      ndp = ndc;
       // unit w finishes at MFMA step h = w * 2 * KST / 16; its exponent and exp2 run one and
       // two steps earlier (clamped to the first step)
-      sdp(nsl, qb ^ 1, ns, ndp, [&](int i) FA_INL {
+      sdp(nsl, qb ^ 1, ns, ndp, sdp_pre, [&](int r) FA_INL { return dvdk_frag(sl, qb, r); }, dvdk_pre,
+          [&](int i) FA_INL {
 #pragma unroll
-        for (int w = 0; w < 16; ++w) {
-          const int h = w * 2 * KST / 16;  // (a unit's stages in order when clamped together)
-          if ((h >= 2 ? h - 2 : 0) == i) pds_a(cs, rv, w);
-          if ((h >= 1 ? h - 1 : 0) == i) pds_b(cs, w);
-          if (h == i) pds_c(cs, cdp, pa, dsa, pt, dt, w);
-        }
-      });
+            for (int w = 0; w < 16; ++w) {
+              const int h = w * 2 * KST / 16;  // (a unit's stages in order when clamped together)
+              if ((h >= 2 ? h - 2 : 0) == i) pds_a(cs, l2, w);
+              if ((h >= 1 ? h - 1 : 0) == i) pds_b(cs, w);
+              if (h == i) pds_c(cs, cdp, pa, dsa, pt, dt, w);
+            }
+          });
     } else {
 #pragma unroll
-      for (int w = 0; w < 16; ++w) pds_a(cs, rv, w);
+      for (int w = 0; w < 16; ++w) pds_a(cs, l2, w);
 #pragma unroll
       for (int w = 0; w < 16; ++w) pds_b(cs, w);
 #pragma unroll
       for (int w = 0; w < 16; ++w) pds_c(cs, cdp, pa, dsa, pt, dt, w);
+#pragma unroll
+      for (int r = 0; r < RD; ++r) dvdk_pre[r] = dvdk_frag(sl, qb, r);
     }
-    dvdk(sl, qb, pa, dsa);
+    // during dV/dK of u: the LSE values of u+1 and -D of u+2, then u+2's first S/dP fragments
+    // (unit u+2 has block qb, in slot n2sl)
+    dvdk(std::integral_constant<bool, !HAS_NEXT>{}, std::integral_constant<bool, !HAS_NEXT>{}, has_next2_tag, sl, qb,
+         pa, dsa, dvdk_pre,
+         [&]() FA_INL {
+           if constexpr (HAS_NEXT) l2c = rowvals(nsl, qb ^ 1);
+           if constexpr (HAS_NEXT2) ndc = neg_d(n2sl, qb);
+         },
+         [&](int r) FA_INL { return sdp_frag(n2sl, qb, r); }, sdp_pre);
   };
 
   // Per query tile: wait for its successor's loads and let every wave see them (everyone is
   // then also done with the tile two back, whose slot the next loads refill), then two units.
   // The slots are restrict-qualified parameters so that the compiler can tell these reads
-  // from the direct loads in flight and does not make them wait.
+  // from the direct loads in flight and does not make them wait.  Unit (qt, 1)'s successors
+  // (qt+1, 0) and (qt+1, 1) are in the next tile's slot, which has been complete since this
+  // tile's barrier.
   f32x16 s0, dp0, s1, dp1;
-  auto tile = [&](auto masked_tag, auto last_tag, int qt, char* __restrict__ cur, char* __restrict__ nxt,
+  // causal: the first two tiles hold this workgroup's diagonal; every later tile is entirely
+  // below it
+  const int qt_m = CAUSAL ? min(n_qt, qt0 + 2) : q_lo;
+  auto tile = [&](auto last_tag, int qt, char* __restrict__ cur, char* __restrict__ nxt,
                   char* __restrict__ dst) FA_INL {
     constexpr bool LAST = decltype(last_tag)::value;
+    const bool masked = qt < qt_m;
     wait_vmcnt<0>();
     lds_barrier();
     if (qt + 2 < n_qt) issue(qt + 2, dst);
     __builtin_amdgcn_sched_barrier(0);
-    unit(masked_tag, std::true_type{}, qt, 0, cur, cur, s0, dp0, s1, dp1);
-    if constexpr (LAST)
-      unit(masked_tag, std::false_type{}, qt, 1, cur, nxt, s1, dp1, s0, dp0);
-    else
-      unit(masked_tag, std::true_type{}, qt, 1, cur, nxt, s1, dp1, s0, dp0);
+    if constexpr (LAST) {
+      unit(masked, std::true_type{}, std::false_type{}, qt, 0, cur, cur, nxt, s0, dp0, s1, dp1);
+      unit(masked, std::false_type{}, std::false_type{}, qt, 1, cur, nxt, nxt, s1, dp1, s0, dp0);
+    } else {
+      unit(masked, std::true_type{}, std::true_type{}, qt, 0, cur, cur, nxt, s0, dp0, s1, dp1);
+      unit(masked, std::true_type{}, std::true_type{}, qt, 1, cur, nxt, nxt, s1, dp1, s0, dp0);
+    }
   };
 
   if (q_lo < n_qt) {
-    // prologue: S/dP of the first unit
+    // prologue: S/dP of the first unit, and the reads the first iteration starts from
     wait_vmcnt<0>();
     lds_barrier();
     s0 = f32x16{};
     dp0 = neg_d(smem, 0);
-    sdp(smem, 0, s0, dp0, [](int) FA_INL {});
+    u32x4 pre[RD];
+#pragma unroll
+    for (int r = 0; r < RD; ++r) pre[r] = sdp_frag(smem, 0, r);
+    sdp(smem, 0, s0, dp0, pre, [&](int r) FA_INL { return sdp_frag(smem, 1, r); }, sdp_pre, [](int) FA_INL {});
+    l2c = rowvals(smem, 0);
+    ndc = neg_d(smem, 1);
     char* c0 = smem;
     char* c1 = smem + SLOT;
     char* c2 = smem + 2 * SLOT;
-    auto run = [&](auto masked_tag, auto last_tag, int qt) FA_INL {
-      tile(masked_tag, last_tag, qt, c0, c1, c2);
+    auto run = [&](auto last_tag, int qt) FA_INL {
+      tile(last_tag, qt, c0, c1, c2);
       char* t = c0;
       c0 = c1;
       c1 = c2;
       c2 = t;
     };
-    // causal: the first two tiles hold this workgroup's diagonal; every later tile is
-    // entirely below it
-    const int qt_m = CAUSAL ? min(n_qt, qt0 + 2) : q_lo;
     int qt = q_lo;
-    for (; qt < qt_m && qt < n_qt - 1; ++qt) run(std::true_type{}, std::false_type{}, qt);
-    for (; qt < n_qt - 1; ++qt) run(std::false_type{}, std::false_type{}, qt);
-    if (qt < qt_m)
-      run(std::true_type{}, std::true_type{}, qt);
-    else
-      run(std::false_type{}, std::true_type{}, qt);
+    for (; qt < n_qt - 1; ++qt) run(std::false_type{}, qt);
+    run(std::true_type{}, qt);
   }
 
-  // ---- epilogue: register i of dKa/dVa[db] <-> key kw0 + (i/4)*8 + g*4 + i%4, column db*32 + c
+  // ---- epilogue: register i of acc[.][db] <-> key kw0 + (i/4)*8 + g*4 + i%4, column db*32 + c
+  reg_fence(acc, true, false);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -383,12 +425,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const int d = db * 32 + c;
       if (PARTIAL) {
         const size_t off = (((size_t)bh * n_qp + piece) * N + kr_) * HD + d;
-        dKp[off] = dKa[db][i] * scale;
-        dVp[off] = dVa[db][i];
+        dKp[off] = acc[0][db][i] * scale;
+        dVp[off] = acc[1][db][i];
       } else {
         const size_t off = kvoff + (size_t)kr_ * HD + d;
-        dK[off] = (uint16_t)(TR::pack(dKa[db][i] * scale, 0.f) & 0xffffu);
-        dV[off] = (uint16_t)(TR::pack(dVa[db][i], 0.f) & 0xffffu);
+        dK[off] = (uint16_t)(TR::pack(acc[0][db][i] * scale, 0.f) & 0xffffu);
+        dV[off] = (uint16_t)(TR::pack(acc[1][db][i], 0.f) & 0xffffu);
       }
     }
 }

@@ -9,6 +9,8 @@
 // same product; the kernels use that freedom to chain accumulators into operands.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -242,6 +244,66 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Written-out MFMAs (v_mfma_f32_32x32x16 bf16/fp16), for kernels that keep accumulators or
+// stationary operands in AGPRs while other MFMA results land in VGPRs for the VALU: the
+// compiler picks one register form for all MFMAs of a kernel, so such a mix is inline
+// assembly.  The compiler does not see these as MFMAs and inserts no wait states for them, so
+// a sequence of them carries its own where needed (CDNA3/CDNA4 dependency rules): kNopBefore
+// waits 2 for VALU writes of its operands (s_nop 1), kNopAfter waits 24 (three s_nop 7) before
+// anything else may touch a result (an 8-pass XDL result needs at most 19 before a VALU,
+// v_accvgpr or memory access).  The waits are in the same statement as the MFMA, so no
+// instruction the compiler places around it can fall inside the window.  A and B are read when
+// an MFMA issues, and an exactly overlapping accumulator chains without wait states.  The
+// library's tests check the windows on the compiled code.
+enum { kNopNone, kNopBefore, kNopAfter };
+#define FA_MFMA_ASM(NOP, TEXT, OUT, ...)                                               \
+  do {                                                                                 \
+    if constexpr (NOP == kNopBefore)                                                   \
+      asm volatile("s_nop 1\n\t" TEXT : OUT : __VA_ARGS__);                            \
+    else if constexpr (NOP == kNopAfter)                                               \
+      asm volatile(TEXT "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : OUT : __VA_ARGS__);      \
+    else                                                                               \
+      asm volatile(TEXT : OUT : __VA_ARGS__);                                          \
+  } while (0)
+template <typename TR, int NOP>  // acc (AGPR) += a b
+__device__ __forceinline__ void mfma_av(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (std::is_same<TR, F16>::value)
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, %0", "+a"(acc), "v"(a), "v"(b));
+  else
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", "+a"(acc), "v"(a), "v"(b));
+}
+template <typename TR, int NOP>  // acc (VGPR) += a b (b in AGPRs)
+__device__ __forceinline__ void mfma_va(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (std::is_same<TR, F16>::value)
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, %0", "+v"(acc), "v"(a), "a"(b));
+  else
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", "+v"(acc), "v"(a), "a"(b));
+}
+template <typename TR, int NOP>  // acc (VGPR) = a b (b in AGPRs)
+__device__ __forceinline__ void mfma_va0(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (std::is_same<TR, F16>::value)
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, 0", "=&v"(acc), "v"(a), "a"(b));
+  else
+    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0", "=&v"(acc), "v"(a), "a"(b));
+}
+#undef FA_MFMA_ASM
+// Ordering point for the registers of `r`: each is an operand here, so no access to them
+// moves across it.  With `nop`, two wait states follow (after VALU or v_accvgpr writes of `r`,
+// before MFMAs read it).  The scheduler also keeps live ranges short around these points.
+template <typename T, int A, int B>
+__device__ __forceinline__ void reg_fence(T (&r)[A][B], bool agpr, bool nop) {
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (agpr)
+        asm volatile("" : "+a"(r[i][j]));
+      else
+        asm volatile("" : "+v"(r[i][j]));
+    }
+  if (nop) asm volatile("s_nop 1" ::: "memory");
 }
 
 // Workgroup barrier that drains only this wave's LDS operations, even while direct

@@ -43,66 +43,6 @@ constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 of the larg
 // that block's list, so the blocks' chains interleave.
 constexpr int kSmMax = 16, kSmRed = 16, kSmExp0 = 17, kSmUnits = 49;
 
-// MFMAs for waves of 64 query rows.  Such a wave needs more than the 256 VGPRs, and the
-// compiler picks one register form for all MFMAs of a kernel, so these are written out: the
-// O accumulators (128 registers at D = 128) and the Q fragments (64) live in AGPRs, which only
-// MFMAs read, while the scores land in VGPRs, which the softmax reads directly.  The compiler
-// does not see these as MFMAs and inserts no wait states for them, so a sequence of them
-// carries its own (CDNA3/CDNA4 dependency rules): the first waits 2 for VALU writes of its
-// operands (s_nop 1), the last waits 24 (three s_nop 7) before anything else may touch a result
-// (an 8-pass XDL result needs at most 19 before a VALU or v_accvgpr access).  The waits are in
-// the same statement as the MFMA, so no instruction the compiler places around it can fall
-// inside the window.  Between them, A and B are read when an MFMA issues and an exactly
-// overlapping accumulator chains without wait states.
-enum { kNopNone, kNopBefore, kNopAfter };
-#define FA_MFMA_ASM(NOP, TEXT, OUT, ...)                                               \
-  do {                                                                                 \
-    if constexpr (NOP == kNopBefore)                                                   \
-      asm volatile("s_nop 1\n\t" TEXT : OUT : __VA_ARGS__);                            \
-    else if constexpr (NOP == kNopAfter)                                               \
-      asm volatile(TEXT "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : OUT : __VA_ARGS__);      \
-    else                                                                               \
-      asm volatile(TEXT : OUT : __VA_ARGS__);                                          \
-  } while (0)
-template <typename TR, int NOP>  // acc (AGPR) += a b
-__device__ __forceinline__ void mfma_av(f32x16& acc, u32x4 a, u32x4 b) {
-  if constexpr (std::is_same<TR, F16>::value)
-    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, %0", "+a"(acc), "v"(a), "v"(b));
-  else
-    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", "+a"(acc), "v"(a), "v"(b));
-}
-template <typename TR, int NOP>  // acc (VGPR) += a b (b in AGPRs)
-__device__ __forceinline__ void mfma_va(f32x16& acc, u32x4 a, u32x4 b) {
-  if constexpr (std::is_same<TR, F16>::value)
-    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, %0", "+v"(acc), "v"(a), "a"(b));
-  else
-    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", "+v"(acc), "v"(a), "a"(b));
-}
-template <typename TR, int NOP>  // acc (VGPR) = a b (b in AGPRs)
-__device__ __forceinline__ void mfma_va0(f32x16& acc, u32x4 a, u32x4 b) {
-  if constexpr (std::is_same<TR, F16>::value)
-    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_f16 %0, %1, %2, 0", "=&v"(acc), "v"(a), "a"(b));
-  else
-    FA_MFMA_ASM(NOP, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0", "=&v"(acc), "v"(a), "a"(b));
-}
-#undef FA_MFMA_ASM
-// Ordering point for the registers of `r`: each is an operand here, so no access to them
-// moves across it.  With `nop`, two wait states follow (after VALU or v_accvgpr writes of `r`,
-// before MFMAs read it).  The scheduler also keeps live ranges short around these points.
-template <typename T, int A, int B>
-__device__ __forceinline__ void reg_fence(T (&r)[A][B], bool agpr, bool nop) {
-#pragma unroll
-  for (int i = 0; i < A; ++i)
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      if (agpr)
-        asm volatile("" : "+a"(r[i][j]));
-      else
-        asm volatile("" : "+v"(r[i][j]));
-    }
-  if (nop) asm volatile("s_nop 1" ::: "memory");
-}
-
 // SPLIT = 2: the workgroup's waves form two groups that own the same query rows and split
 // the K/V range in two contiguous halves (an on-chip split of the key range); each group runs
 // the online softmax over its half and the halves merge through LDS at the end, exactly, by

@@ -1,9 +1,10 @@
-"""Data hazards around the forward's written-out MFMAs (host-side check of the gfx950 assembly).
+"""Data hazards around the written-out MFMAs (host-side check of the gfx950 assembly).
 
-The forward kernel for waves of 64 query rows issues its MFMAs as inline assembly (accumulators
-and Q fragments in AGPRs, scores in VGPRs).  The compiler inserts no wait states for them, so
-the kernel places its own.  This test compiles the forward to assembly with the library's
-flags and walks every control-flow path from each written-out MFMA:
+The forward kernel for waves of 64 query rows and the dK/dV pass issue MFMAs as inline assembly
+(accumulators and stationary operands in AGPRs, scores in VGPRs).  The compiler inserts no
+wait states for them, so the kernels place their own.  This test compiles the sources to
+assembly with the library's flags and walks every control-flow path from each written-out
+MFMA:
 
   * no instruction other than an MFMA chaining on exactly the same accumulator may read or
     write the MFMA's destination within 19 wait states (an 8-pass XDL result needs at most 19
@@ -150,34 +151,44 @@ def _check(body):
     return problems, n_asm
 
 
-@pytest.fixture(scope="module")
-def forward_asm(tmp_path_factory):
+def _compile(tmp_path_factory, src):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "fa_fwd.s"
-    cmd = [hipcc, *_build.common_flags(), *_build.DEVICE_FLAGS.get("fa_fwd.hip", []), "--cuda-device-only",
-           "-S", os.path.join(_build.CSRC, "fa_fwd.hip"), "-o", str(out)]
+    out = tmp_path_factory.mktemp("asm") / (src + ".s")
+    cmd = [hipcc, *_build.common_flags(), *_build.DEVICE_FLAGS.get(src, []), "--cuda-device-only",
+           "-S", os.path.join(_build.CSRC, src), "-o", str(out)]
     cmd = [c for c in cmd if c != "-fPIC"]
     p = subprocess.run(cmd, capture_output=True, text=True)
     assert p.returncode == 0, p.stderr[-2000:]
     return out.read_text()
 
 
-def test_written_out_mfmas_have_their_wait_states(forward_asm):
-    kernels = _functions(forward_asm, r"fwd_kernel")
-    assert kernels, "no forward kernels in the assembly"
+# (source, kernels that use written-out MFMAs, kernels that must not spill)
+SOURCES = [("fa_fwd.hip", r"fwd_kernel"), ("fa_bwd.hip", r"bwd_dkdv_kernel")]
+
+
+@pytest.fixture(scope="module", params=SOURCES, ids=[s for s, _ in SOURCES])
+def compiled(request, tmp_path_factory):
+    src, pattern = request.param
+    return _compile(tmp_path_factory, src), pattern
+
+
+def test_written_out_mfmas_have_their_wait_states(compiled):
+    asm, pattern = compiled
+    kernels = _functions(asm, pattern)
+    assert kernels, "no kernels in the assembly"
     total_asm = 0
     for name, body in kernels.items():
         problems, n_asm = _check(body)
         total_asm += n_asm
         assert not problems, f"{name}: " + "; ".join(problems[:5])
-    # the 64-row kernels (bf16/fp16 x D 64/128 x causal or not) use them
     assert total_asm > 0
 
 
-def test_forward_kernels_do_not_spill(forward_asm):
-    for name, body in _functions(forward_asm, r"fwd_kernel").items():
+def test_kernels_do_not_spill(compiled):
+    asm, pattern = compiled
+    for name, body in _functions(asm, pattern).items():
         assert "scratch_store" not in body and "scratch_load" not in body, f"{name} spills to scratch"
 
 
