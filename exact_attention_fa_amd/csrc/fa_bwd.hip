@@ -297,9 +297,15 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const int db = i >> 2, t2 = (i >> 1) & 1;
       const u32x4 a = (i & 1) ? dsa[t2] : pa[t2];
       f32x16& o = acc[(i & 1) ? 0 : 1][db];
-      if (i == 0 || decltype(rare_tag)::value)  // (P and dS were packed by the VALU just before)
+      // (P and dS were packed by the VALU just before the first MFMA; after the last one of the
+      // tail unit the epilogue reads the accumulators)
+      constexpr bool RARE = decltype(rare_tag)::value, TAIL = decltype(tail_tag)::value;
+      const bool before = i == 0 || RARE, after = TAIL && i == NS - 1;
+      if (before && after)
+        mfma_av<TR, kNopBoth>(o, a, ring[i % (RD + 1)]);
+      else if (before)
         mfma_av<TR, kNopBefore>(o, a, ring[i % (RD + 1)]);
-      else if (decltype(tail_tag)::value && i == NS - 1)  // the epilogue reads the accumulators
+      else if (after)
         mfma_av<TR, kNopAfter>(o, a, ring[i % (RD + 1)]);
       else
         mfma_av<TR, kNopNone>(o, a, ring[i % (RD + 1)]);

@@ -252,20 +252,22 @@ __device__ __forceinline__ void lds_barrier() {
 // assembly.  The compiler does not see these as MFMAs and inserts no wait states for them, so
 // a sequence of them carries its own where needed (CDNA3/CDNA4 dependency rules): kNopBefore
 // waits 2 for VALU writes of its operands (s_nop 1), kNopAfter waits 24 (three s_nop 7) before
-// anything else may touch a result (an 8-pass XDL result needs at most 19 before a VALU,
+// anything else may touch a result, kNopBoth does both (an 8-pass XDL result needs at most 19 before a VALU,
 // v_accvgpr or memory access).  The waits are in the same statement as the MFMA, so no
 // instruction the compiler places around it can fall inside the window.  A and B are read when
 // an MFMA issues, and an exactly overlapping accumulator chains without wait states.  The
 // library's tests check the windows on the compiled code.
-enum { kNopNone, kNopBefore, kNopAfter };
-#define FA_MFMA_ASM(NOP, TEXT, OUT, ...)                                               \
-  do {                                                                                 \
-    if constexpr (NOP == kNopBefore)                                                   \
-      asm volatile("s_nop 1\n\t" TEXT : OUT : __VA_ARGS__);                            \
-    else if constexpr (NOP == kNopAfter)                                               \
-      asm volatile(TEXT "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : OUT : __VA_ARGS__);      \
-    else                                                                               \
-      asm volatile(TEXT : OUT : __VA_ARGS__);                                          \
+enum { kNopNone, kNopBefore, kNopAfter, kNopBoth };
+#define FA_MFMA_ASM(NOP, TEXT, OUT, ...)                                                      \
+  do {                                                                                        \
+    if constexpr (NOP == kNopBefore)                                                          \
+      asm volatile("s_nop 1\n\t" TEXT : OUT : __VA_ARGS__);                                   \
+    else if constexpr (NOP == kNopAfter)                                                      \
+      asm volatile(TEXT "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : OUT : __VA_ARGS__);             \
+    else if constexpr (NOP == kNopBoth)                                                       \
+      asm volatile("s_nop 1\n\t" TEXT "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : OUT : __VA_ARGS__); \
+    else                                                                                      \
+      asm volatile(TEXT : OUT : __VA_ARGS__);                                                 \
   } while (0)
 template <typename TR, int NOP>  // acc (AGPR) += a b
 __device__ __forceinline__ void mfma_av(f32x16& acc, u32x4 a, u32x4 b) {
