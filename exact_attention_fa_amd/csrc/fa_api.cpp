@@ -75,7 +75,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long long N, long long D) {
   BwdWorkspace w{};
   const size_t rows = (size_t)B * (size_t)Hq * (size_t)N;
-  w.n_qp = bwd_query_pieces(B, Hq, N);
+  w.n_qp = bwd_query_pieces(B, Hq, Hkv, N, D);
   w.n_kp = bwd_key_pieces(B, Hq, N, D);
   w.partial_dkdv = Hq != Hkv || w.n_qp > 1;
   size_t off = 0;

@@ -50,7 +50,7 @@ struct BwdWorkspace {
   size_t total;
 };
 // Pieces for grids too small to occupy every CU (depend on the shape only).
-int bwd_query_pieces(long long B, long long Hq, long long N);
+int bwd_query_pieces(long long B, long long Hq, long long Hkv, long long N, long long D);
 int bwd_key_pieces(long long B, long long Hq, long long N, long long D);
 BwdWorkspace bwd_workspace_layout(long long B, long long Hq, long long Hkv, long long N, long long D);
 
