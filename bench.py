@@ -14,6 +14,8 @@ Prints ONE JSON line on stdout:
                   on the stream it is launched on, against the MFMA peak; `traffic` is its HBM
                   bytes per launch from the committed hardware-counter summary under profiles/,
                   or null when the kernel source has changed since the counters were taken
+  hbm             the memory-bound stage (the backward preprocess): algorithmic bytes per
+                  launch over its HIP-event time, against the HBM peak
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
 
 FLOP convention: forward 4*B*H*N^2*D, backward 10*B*H*N^2*D (five N x N x D products,
@@ -251,6 +253,14 @@ def main():
                     "traffic": measured_traffic(dominant, args.workload), "avg_ms": round(avg[dominant], 4)}
     else:  # pragma: no cover - the contractions dominate every listed workload
         roofline = None
+    # The memory-bound stage: the preprocess reads O and dO (input dtype) and the LSE, and
+    # writes -D and LSE*log2(e), all fp32 per row.
+    rows = B * Hq * N
+    pre_bytes = rows * (2 * D * (2 if shape.dtype in ("bf16", "fp16") else 4) + 4 + 8)
+    pre_gbs = pre_bytes / (avg["bwd_preprocess"] * 1e-3) / 1e9
+    hbm = {"kernel": "bwd_preprocess", "bound": "hbm", "achieved": round(pre_gbs, 1), "peak": PEAK_HBM_GBS,
+           "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": pre_bytes,
+           "avg_ms": round(avg["bwd_preprocess"], 4)}
 
     out = {
         "metric": METRIC,
@@ -275,6 +285,7 @@ def main():
         "kernel_avg_ms": {kname: round(val, 4) for kname, val in avg.items()},
         "kernel_median_ms": {kname: round(val, 4) for kname, val in med.items()},
         "roofline": roofline,
+        "hbm": hbm,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
