@@ -11,9 +11,9 @@
 // through LDS and a bitwise-deterministic result).
 //
 // dK/dV pass: a workgroup (4 waves) owns 128 keys of one query head, a wave owns 32 of them;
-// the K and V tiles stay in LDS.  64-query tiles of Q and dO, with the per-row LSE*log2(e)
-// and D, stream through a double-buffered LDS by direct global->LDS loads issued one tile
-// ahead.  Per query tile, per wave and per 32-query block: S = Q K^T and dP = dO V^T on
+// its K and V rows stay in registers.  64-query tiles of Q and dO, with the per-row
+// LSE*log2(e) and D, stream through a triple-buffered LDS by direct global->LDS loads issued
+// two tiles ahead (first read one tile ahead, by the pipelined S/dP).  Per query tile, per wave and per 32-query block: S = Q K^T and dP = dO V^T on
 // v_mfma_f32_32x32x16 with the key as the accumulator column, so each lane owns one key;
 // register 8t+j of the block is query 16t + 8g + j (row permutation of the Q/dO operand),
 // which is exactly the k-slot order of the A operand of dV += P^T dO and dK += dS^T Q, so
@@ -75,8 +75,9 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
 // ---------------------------------------------------------------- dK, dV
 // Key-stationary: a workgroup (4 waves) owns 128 keys of one query head, a wave owns 32.  The
 // wave's K and V rows are loaded once into registers (the B operands of S = Q K^T and
-// dP = dO V^T).  64-query tiles of Q and dO with their LSE*log2(e) and D stream through a
-// triple-buffered LDS by direct loads issued two tiles ahead, one barrier per tile.  Work is
+// dP = dO V^T; in AGPRs, with the dK/dV accumulators).  64-query tiles of Q and dO with their
+// LSE*log2(e) and D stream through a triple-buffered LDS by direct loads issued two tiles
+// ahead, one barrier per tile.  Work is
 // done in units of 32 queries, software-pipelined inside the wave: while the MFMAs of S and
 // dP of unit u+1 run, the VALU forms P and dS of unit u; then the MFMAs of dV += P^T dO and
 // dK += dS^T Q of unit u run with dO and Q read transposed from LDS.  Query rows past the
