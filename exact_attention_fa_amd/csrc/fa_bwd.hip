@@ -45,30 +45,45 @@ constexpr int kDqBC = 32;     // dQ kernel: keys per K/V tile
 // ---------------------------------------------------------------- preprocess
 // Dl[row] = -D[row] = -sum_d dO[row][d] * O[row][d] (fp32, stored negated: it is the
 // accumulator input of the dK/dV pass's dP MFMAs) and L2[row] = LSE[row] * log2(e) (the
-// exponent offset of the base-2 recompute of P).
+// exponent offset of the base-2 recompute of P).  HBM-bound: HD/8 threads share a row, 16
+// bytes of O and of dO each; a thread keeps the loads of kPreRows rows in flight, and at most
+// kPreBlocks workgroups stride over the rows (streaming reads on this GPU reach their best
+// rate with a few thousand resident workgroups, not one short-lived workgroup per 64 rows).
+constexpr int kPreRows = 2, kPreBlocks = 2048;
 template <typename TR, int HD>
 __global__ void __launch_bounds__(kThreads)
 bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                const float* __restrict__ LSE, float* __restrict__ Dl, float* __restrict__ L2, long long rows) {
   constexpr int TPR = HD / 8;          // threads per row, 8 elements each
-  constexpr int RPB = kThreads / TPR;  // rows per block
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  constexpr int RPP = kThreads / TPR;  // rows per pass of the block
   const int part = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 o = ld16(O + row * HD + part * 8);
-    const u32x4 d = ld16(dO + row * HD + part * 8);
+  const long long stride = (long long)gridDim.x * RPP * kPreRows;
+  for (long long row0 = (long long)blockIdx.x * RPP * kPreRows + threadIdx.x / TPR; row0 - threadIdx.x / TPR < rows;
+       row0 += stride) {
+    u32x4 o[kPreRows], d[kPreRows];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = fmaf(TR::lo(o[w]), TR::lo(d[w]), acc);
-      acc = fmaf(TR::hi(o[w]), TR::hi(d[w]), acc);
+    for (int u = 0; u < kPreRows; ++u) {
+      const long long row = row0 + (long long)u * RPP;  // each pass reads RPP consecutive rows
+      const bool ok = row < rows;
+      o[u] = ld16_if(O + (ok ? row : 0) * HD + part * 8, ok);
+      d[u] = ld16_if(dO + (ok ? row : 0) * HD + part * 8, ok);
     }
-  }
 #pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) {
-    Dl[row] = -acc;
-    L2[row] = LSE[row] * kLog2e;
+    for (int u = 0; u < kPreRows; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(TR::lo(o[u][w]), TR::lo(d[u][w]), acc);
+        acc = fmaf(TR::hi(o[u][w]), TR::hi(d[u][w]), acc);
+      }
+#pragma unroll
+      for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      const long long row = row0 + (long long)u * RPP;
+      if (row < rows && part == 0) {
+        Dl[row] = -acc;
+        L2[row] = LSE[row] * kLog2e;
+      }
+    }
   }
 }
 
@@ -816,8 +831,9 @@ template <typename TR, int HD>
 hipError_t pre_t(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
   const long long rows = a.B * a.Hq * a.N;
-  constexpr int RPB = kThreads / (HD / 8);
-  const long long blocks = (rows + RPB - 1) / RPB;
+  constexpr int RPB = kThreads / (HD / 8) * kPreRows;
+  const long long need = (rows + RPB - 1) / RPB;
+  const long long blocks = need < kPreBlocks ? need : kPreBlocks;
   hipLaunchKernelGGL((bwd_pre_kernel<TR, HD>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse,
                      reinterpret_cast<float*>(a.ws + w.delta), reinterpret_cast<float*>(a.ws + w.lse2), rows);
