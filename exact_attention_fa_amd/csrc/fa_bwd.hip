@@ -123,7 +123,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
 
-  int job = xcd_remap(blockIdx.x, gridDim.x);
+  int job = CAUSAL && !snake ? xcd_remap_interleaved(blockIdx.x, gridDim.x, n_kt * n_qp)
+                             : xcd_remap(blockIdx.x, gridDim.x);
   // Small grids cut the query range of each key block into n_qp pieces, one workgroup each,
   // whose partials the postprocess sums (PARTIAL).
   const int piece = job % n_qp;
@@ -501,7 +502,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wv = wave % GW;   // wave within the group
   const int c = lane & 31, g = lane >> 5;
 
-  int job = xcd_remap(blockIdx.x, gridDim.x);
+  int job = CAUSAL && !snake ? xcd_remap_interleaved(blockIdx.x, gridDim.x, n_qt * (PART ? n_kp : 1))
+                             : xcd_remap(blockIdx.x, gridDim.x);
   int part = 0;  // piece of the key range (PART)
   if constexpr (PART) {
     part = job % n_kp;

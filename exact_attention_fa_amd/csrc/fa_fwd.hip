@@ -98,7 +98,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   char* const sK = smem + grp * ((NBK + NB) * TILE);
   char* const sV = sK + NBK * TILE;
 
-  int job = xcd_remap(blockIdx.x, gridDim.x);
+  int job = CAUSAL && !snake ? xcd_remap_interleaved(blockIdx.x, gridDim.x, n_qt * (PART ? n_part : 1))
+                             : xcd_remap(blockIdx.x, gridDim.x);
   int part = 0;  // piece of the key range (PART)
   if constexpr (PART) {
     part = job % n_part;
