@@ -474,7 +474,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     } else {
       wait_vmcnt<0>();
     }
-    lds_barrier();  // ... and everyone's; everyone is also done with step j-1's buffers
+    dma_barrier();  // ... and everyone's; everyone is also done with step j-1's buffers
     if (need) {       // the max moved in the previous step: rescale O (rare)
       scale_acc();
       need = false;
