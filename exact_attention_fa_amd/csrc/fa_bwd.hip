@@ -438,6 +438,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 
   // ---- epilogue: register i of acc[.][db] <-> key kw0 + (i/4)*8 + g*4 + i%4, column db*32 + c
+  // (each store instruction covers 64 or 128 contiguous bytes of two rows; staging the rows
+  // through LDS for whole-row stores, as the forward and dQ passes do, measured no faster)
   reg_fence(acc, true, false);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -767,17 +769,30 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     return;
   }
-  if (qi < N) {
-    uint16_t* const qrow = dQ + (size_t)bh * N * HD + (size_t)qi * HD;
+  // dQ rows go out through LDS, whole rows per store instruction (stage_row, store_staged).
+  // Eight waves of one group need more than the K/V buffers hold: they stage the two halves
+  // of their columns one after the other.
+  constexpr int PASSES = SPLIT == 2 || GW * 32 * HD * 2 <= (int)sizeof(smem) ? 1 : 2;
+  constexpr int HDP = HD / PASSES;  // columns per pass
+  char* qs;
+  if constexpr (SPLIT == 2) {
+    qs = smem + wv * (64 * 16 * DB * 4);  // the hand-off region this wave has just read
+  } else {
+    lds_store_barrier();                  // every wave is done with the K/V buffers
+    qs = smem + wv * (32 * HDP * 2);
+  }
+  static_assert(32 * HDP * 2 <= (SPLIT == 2 ? 64 * 16 * DB * 4 : (int)sizeof(smem) / GW), "dQ rows must fit the region");
+  u32x2 w[DB][4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = db * 32 + i4 * 8 + g * 4;
-        const u32x2 w = {TR::pack(acc[db][i4 * 4 + 0] * scale, acc[db][i4 * 4 + 1] * scale),
-                         TR::pack(acc[db][i4 * 4 + 2] * scale, acc[db][i4 * 4 + 3] * scale)};
-        *reinterpret_cast<u32x2*>(qrow + d) = w;
-      }
+    for (int i4 = 0; i4 < 4; ++i4)
+      w[db][i4] = u32x2{TR::pack(acc[db][i4 * 4 + 0] * scale, acc[db][i4 * 4 + 1] * scale),
+                        TR::pack(acc[db][i4 * 4 + 2] * scale, acc[db][i4 * 4 + 3] * scale)};
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    stage_row<HDP>(qs, c, g, reinterpret_cast<const u32x2(&)[HDP / 32][4]>(w[p * (DB / PASSES)]));
+    store_staged<HDP * 2, 32, HD * 2>(qs, dQ + ((size_t)bh * N + qw0) * HD + p * HDP, N - qw0, lane);
   }
 }
 

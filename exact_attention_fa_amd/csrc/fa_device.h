@@ -184,6 +184,42 @@ __device__ __forceinline__ void dma_to_lds(BufRes res, uint32_t voff, uint32_t s
 __device__ __forceinline__ u32x4 lds_ld128(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void lds_st128(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Row-major output tiles staged through LDS.  In the accumulator layouts a store instruction
+// covers 2 to 8 bytes of each of 32 rows per lane; with every CU storing its tile at about the
+// same moment such partial-line writes cost several microseconds per workgroup.  A wave
+// therefore writes its rows into a private LDS region (rows of RB bytes, their 16-byte chunks
+// XOR-swizzled by the row index, so that column-wise writes over consecutive rows and
+// row-wise reads spread over the banks) and stores them back as 16 bytes per lane, 1 KB of
+// consecutive rows per instruction.
+template <int RB>
+__device__ __forceinline__ uint32_t stage_off(int r, int ch) {
+  constexpr int CH = RB / 16;  // 16-byte chunks per row
+  return (uint32_t)(r * RB + ((ch ^ (r & (CH - 1))) << 4));
+}
+// 16-bit rows of HD columns: lane (c, g) puts row r's columns db*32 + i4*8 + g*4 .. +3
+// (two packed pairs, w[db][i4]).
+template <int HD>
+__device__ __forceinline__ void stage_row(char* region, int r, int g, const u32x2 (&w)[HD / 32][4]) {
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      *reinterpret_cast<u32x2*>(region + stage_off<HD * 2>(r, db * 4 + i4) + g * 8) = w[db][i4];
+}
+// Copies the region's first R rows to dst, whose rows are STRIDE bytes apart (a staged row may
+// be part of a destination row); rows >= n_valid are skipped.
+template <int RB, int R, int STRIDE = RB>
+__device__ __forceinline__ void store_staged(const char* region, void* dst, int n_valid, int lane) {
+  constexpr int CH = RB / 16, RPI = 64 / CH;  // chunks per row, rows per instruction
+  static_assert(R % RPI == 0, "whole instructions");
+#pragma unroll
+  for (int k = 0; k < R / RPI; ++k) {
+    const int r = k * RPI + lane / CH, ch = lane % CH;
+    const u32x4 v = lds_ld128(region + stage_off<RB>(r, ch));
+    if (r < n_valid) *reinterpret_cast<u32x4*>(static_cast<char*>(dst) + (size_t)r * STRIDE + ch * 16) = v;
+  }
+}
+
 // Lane offsets of the transposed-operand read (see lds_tr8): rows lr and lr + 4, column lc.
 struct TrLane {
   uint32_t r0, r4;

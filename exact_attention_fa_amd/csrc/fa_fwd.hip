@@ -638,45 +638,30 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       if (g == 0) Lp[row] = l_tot > 0.f ? m_run[qb] * scale + __logf(l_tot) : -INFINITY;
     }
   } else {
-    // O rows pass through LDS so that every store instruction writes whole rows: in the
-    // accumulator layout a store covers only 16 bytes of each of 32 rows, and with every CU
-    // storing its tile at about the same time such partial-line writes took 3-4 us per
-    // workgroup.  Each wave packs its rows into a private LDS region (16-byte chunks of a row
-    // XOR-swizzled by the row index, so that the writes of 32 rows and the reads of whole rows
-    // are free of bank conflicts), then reads them back as 16 bytes per lane, 1 KB of
-    // consecutive rows per instruction.
-    constexpr int RB = HD * 2, CH = RB / 16, RPI = 64 / CH;  // bytes per row, chunks per row, rows per read
+    // O rows go out through LDS, whole rows per store instruction (stage_row, store_staged).
     char* ob;
     if constexpr (SPLIT == 2) {
       ob = smem + wv * (64 * XW * 4);  // the hand-off region this wave has just read
     } else {
       lds_store_barrier();             // every wave is done with the K/V buffers
-      ob = sK + wv * (RW * RB);
+      ob = sK + wv * (RW * HD * 2);
     }
-    static_assert(RW * RB <= (SPLIT == 2 ? 64 * XW * 4 : NBK * TILE / GW), "O rows must fit the region");
+    static_assert(RW * HD * 2 <= (SPLIT == 2 ? 64 * XW * 4 : NBK * TILE / GW), "O rows must fit the region");
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float l_tot = pair_sum(l_run[qb]);
       const float inv = 1.f / l_tot;
-      const int r = qb * 32 + c;
+      u32x2 w[DB][4];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int ch = db * 4 + i4;
-          const u32x2 w = {TR::pack(acc[qb][db][i4 * 4 + 0] * inv, acc[qb][db][i4 * 4 + 1] * inv),
-                           TR::pack(acc[qb][db][i4 * 4 + 2] * inv, acc[qb][db][i4 * 4 + 3] * inv)};
-          *reinterpret_cast<u32x2*>(ob + r * RB + ((ch ^ (r & (CH - 1))) << 4) + g * 8) = w;
-        }
+        for (int i4 = 0; i4 < 4; ++i4)
+          w[db][i4] = u32x2{TR::pack(acc[qb][db][i4 * 4 + 0] * inv, acc[qb][db][i4 * 4 + 1] * inv),
+                            TR::pack(acc[qb][db][i4 * 4 + 2] * inv, acc[qb][db][i4 * 4 + 3] * inv)};
+      stage_row<HD>(ob, qb * 32 + c, g, w);
       if (qi[qb] < N && g == 0) LSE[(size_t)bh * N + qi[qb]] = m_run[qb] * scale + __logf(l_tot);
     }
-    uint16_t* const ow = O + ((size_t)bh * N + qw0) * HD;  // this wave's first row
-#pragma unroll
-    for (int k = 0; k < RW / RPI; ++k) {
-      const int r = k * RPI + lane / CH, ch = lane % CH;
-      const u32x4 v = lds_ld128(ob + r * RB + ((ch ^ (r & (CH - 1))) << 4));
-      if (qw0 + r < N) *reinterpret_cast<u32x4*>(ow + (size_t)r * HD + ch * 8) = v;
-    }
+    store_staged<HD * 2, RW>(ob, O + ((size_t)bh * N + qw0) * HD, N - qw0, lane);
   }
 }
 
