@@ -93,7 +93,7 @@ __device__ __forceinline__ u32x4 ld16_if(const uint16_t* p, bool ok) {
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Remap the hardware
 // id so that consecutive logical jobs (the tiles of one head, which stream the same
 // K/V) run on the same XCD and share its L2.  A bijection for any grid size.
-__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   constexpr int NXCD = 8;
   const int q = nblk / NXCD, r = nblk % NXCD;
   const int xcd = bid % NXCD, slot = bid / NXCD;
@@ -108,7 +108,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // jobs as xcd_remap, but when its range holds h > 1 whole heads of `per_head` jobs each, slot s
 // takes job s / h of head s % h: the heads advance together, and four consecutive slots span
 // at most two neighbouring tiles instead of four.
-__device__ __forceinline__ int xcd_remap_interleaved(int bid, int nblk, int per_head) {
+__host__ __device__ __forceinline__ int xcd_remap_interleaved(int bid, int nblk, int per_head) {
   constexpr int NXCD = 8;
   const int q = nblk / NXCD, r = nblk % NXCD;
   const int xcd = bid % NXCD, slot = bid / NXCD;
@@ -124,7 +124,7 @@ __device__ __forceinline__ int xcd_remap_interleaved(int bid, int nblk, int per_
 // consecutive heads alternate heaviest-first and lightest-first, so the two workgroups a CU
 // receives from consecutive heads add up to about the same work on every CU.  Otherwise the
 // grid runs in several rounds and heaviest-first lets the dispatcher balance as slots free up.
-__device__ __forceinline__ int causal_tile(int idx, int head, int n, int snake) {
+__host__ __device__ __forceinline__ int causal_tile(int idx, int head, int n, int snake) {
   return (snake && (head & 1)) ? idx : n - 1 - idx;
 }
 // Whole grid resident at once: every workgroup has a slot on some CU from the start.
