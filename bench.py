@@ -31,6 +31,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -65,11 +66,22 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(rel, text):
+    """The source without comments and blank lines: editing a comment leaves the kernel, and
+    so the counters taken on it, unchanged."""
+    if rel.endswith(".py"):
+        text = re.sub(r"#[^\n]*", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(rel, f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -293,8 +293,11 @@ __device__ __forceinline__ void pipelined(LoadF&& load, ComputeF&& compute) {
 
 // ---------------------------------------------------------------- synchronisation
 
-// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations only.  (HIP's
-// __syncthreads also drains every outstanding global load, store and atomic.)
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations, which include
+// its direct global->LDS loads (the LDS-scoped release fence waits for those too, vmcnt(0)),
+// but not for its global stores or ordinary loads.  (HIP's __syncthreads also drains every
+// outstanding global load, store and atomic.)  Where later tiles' direct loads should stay
+// in flight across the barrier, dma_barrier below is the one to use.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
