@@ -49,6 +49,7 @@ SMALL = [
     (1, 6, 2, 333, 128),     # GQA 3:1, ragged
     (1, 2, 2, 640, 64),      # several whole tiles
     (2, 4, 4, 517, 128),     # MHA, ragged, B=2
+    (1, 16, 1, 300, 128),    # MQA, sixteen query heads summed into one K/V gradient
 ]
 
 
