@@ -17,6 +17,8 @@ Prints ONE JSON line on stdout:
   hbm             the memory-bound stage (the backward preprocess): algorithmic bytes per
                   launch over its HIP-event time, against the HBM peak
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
+  kernel_*_ms     per-kernel average, median, minimum and maximum over the timed steps
+  gpu_clock       the shader clock rocm-smi reports before the warmup and after the timed steps
 
 FLOP convention: forward 4*B*H*N^2*D, backward 10*B*H*N^2*D (five N x N x D products,
 including the recompute of S), halved when causal.
@@ -33,6 +35,7 @@ import os
 import platform
 import re
 import statistics
+import subprocess
 import sys
 import time
 
@@ -100,6 +103,19 @@ def measured_traffic(kernel, workload):
     if kv.get("source_sha256_16") != source_hash(kernel) or "hbm_bytes_per_launch" not in kv:
         return None
     return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def gpu_clock():
+    """The shader clock as rocm-smi reports it (a read-only query, outside any timed region),
+    or None where the tool is missing or its output cannot be read."""
+    try:
+        r = subprocess.run([os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "rocm-smi"), "-g", "--json"],
+                           capture_output=True, text=True, timeout=15)
+        d = json.loads(r.stdout[r.stdout.index("{"):])
+        card = d[sorted(d)[0]]
+        return {k.strip(" :"): v for k, v in card.items() if "sclk" in k.lower()} or None
+    except Exception:  # the clock is context for the numbers, never a reason to fail the run
+        return None
 
 
 def copy_calibration(nbytes):
@@ -225,6 +241,7 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
+    clock_before = gpu_clock()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -237,6 +254,7 @@ def main():
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock_after = gpu_clock()
 
     per_kernel = {kname: [] for kname in kernels}
     step_ms = []
@@ -296,6 +314,9 @@ def main():
         "fwd_bwd_pct_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
         "kernel_avg_ms": {kname: round(val, 4) for kname, val in avg.items()},
         "kernel_median_ms": {kname: round(val, 4) for kname, val in med.items()},
+        "kernel_min_ms": {kname: round(min(vals), 4) for kname, vals in per_kernel.items()},
+        "kernel_max_ms": {kname: round(max(vals), 4) for kname, vals in per_kernel.items()},
+        "gpu_clock": {"before": clock_before, "after": clock_after},
         "roofline": roofline,
         "hbm": hbm,
         "cpu_baseline": None,
