@@ -25,6 +25,8 @@ including the recompute of S), halved when causal.
 
 `--copy-calibration BYTES` instead runs a plain device-to-device copy of BYTES bytes five
 times (the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
+`--ceilings` instead measures what the GPU sustains on plain library work (8192^3 bf16 and
+fp16 GEMMs, 2 GiB HBM read and copy), context for the roofline fractions, and exits.
 """
 from __future__ import annotations
 
@@ -103,6 +105,43 @@ def measured_traffic(kernel, workload):
     if kv.get("source_sha256_16") != source_hash(kernel) or "hbm_bytes_per_launch" not in kv:
         return None
     return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def machine_ceilings():
+    """What this GPU sustains on plain library work, as context for the roofline fractions:
+    a large bf16 and fp16 GEMM (torch.matmul, i.e. hipBLASLt) and HBM streaming (a reduction
+    that reads 2 GiB, and a 2 GiB device copy).  One JSON line."""
+    import torch
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    out = {"clock_before": gpu_clock()}
+    n = 8192
+    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        a = torch.randn(n, n, device="cuda").to(dt)
+        b = torch.randn(n, n, device="cuda").to(dt).contiguous()
+        t = timed(lambda: torch.matmul(a, b), 40)
+        out[f"gemm_{name}_{n}_tflops"] = round(2 * n ** 3 / t / 1e12, 1)
+        out[f"gemm_{name}_pct_of_spec"] = round(100 * 2 * n ** 3 / t / 1e12 / PEAK_MFMA_TFLOPS, 1)
+        del a, b
+    x = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda")  # 2 GiB
+    t = timed(lambda: x.sum(dtype=torch.float32), 20)
+    out["hbm_read_gbs"] = round(x.numel() * 2 / t / 1e9, 1)
+    y = torch.empty_like(x)
+    t = timed(lambda: y.copy_(x), 20)
+    out["hbm_copy_read_plus_write_gbs"] = round(2 * x.numel() * 2 / t / 1e9, 1)
+    out["clock_after"] = gpu_clock()
+    print(json.dumps(out), flush=True)
 
 
 def gpu_clock():
@@ -186,6 +225,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--ceilings", action="store_true", help="measure library GEMM and HBM rates and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -195,6 +235,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.ceilings:
+        machine_ceilings()
         return
 
     import torch
