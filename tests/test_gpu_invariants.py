@@ -183,3 +183,28 @@ def test_backward_stages_equal_fused_call(torch_fa):
     fa.fa_bwd_postprocess(dk2, dv2, ws, 8)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+def test_concurrent_streams_match_one_stream(torch_fa):
+    """The library keeps no mutable global state: the same calls enqueued on two streams at
+    once (separate outputs and workspaces) give the bits of a single-stream run."""
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    shapes = [Shape(2, 8, 2, 1500, 128, "bf16", True), Shape(1, 4, 4, 2100, 64, "fp16", False)]
+    data = [inputs(s, 31 + i) for i, s in enumerate(shapes)]
+    ref = []
+    for (q, k, v, do), s in zip(data, shapes):
+        o, lse = fa.fa_fwd(q, k, v, causal=s.causal)
+        ref.append((o, lse, *fa.fa_bwd(q, k, v, o, do, lse, causal=s.causal)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    out = [None, None]
+    for rep in range(3):
+        for i, ((q, k, v, do), s) in enumerate(zip(data, shapes)):
+            with torch.cuda.stream(streams[i]):
+                o, lse = fa.fa_fwd(q, k, v, causal=s.causal)
+                out[i] = (o, lse, *fa.fa_bwd(q, k, v, o, do, lse, causal=s.causal))
+        torch.cuda.synchronize()
+        for i in range(2):
+            for a, b in zip(out[i], ref[i]):
+                assert torch.equal(a, b), f"stream {i}, repetition {rep}"
