@@ -208,3 +208,46 @@ def test_concurrent_streams_match_one_stream(torch_fa):
         for i in range(2):
             for a, b in zip(out[i], ref[i]):
                 assert torch.equal(a, b), f"stream {i}, repetition {rep}"
+
+
+def test_graph_replay_matches_eager(torch_fa):
+    """fa_fwd and the fa_bwd stages captured in a HIP graph: every replay, with new inputs
+    copied in and eager work in between, gives the bits of the eager calls."""
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    shape = Shape(1, 8, 2, 1200, 128, "bf16", True)
+    B, Hq, Hkv, N, D = shape.B, shape.Hq, shape.Hkv, shape.N, shape.D
+    q, k, v, do = (t.clone() for t in inputs(shape, 41))
+    o, lse = torch.empty_like(q), torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fa.fa_fwd(q, k, v, causal=True, out=o, lse=lse)
+        fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
+        fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=True)
+        fa.fa_bwd_dq(q, k, v, do, dq, ws, causal=True)
+        fa.fa_bwd_postprocess(dk, dv, ws, Hq)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new = inputs(shape, 50 + rep)
+        for dst, src in zip((q, k, v, do), new):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (o, lse, dq, dk, dv)]
+        e_o, e_l = fa.fa_fwd(q, k, v, causal=True)
+        e_g = fa.fa_bwd(q, k, v, e_o, do, e_l, causal=True)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, (e_o, e_l, *e_g)):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
