@@ -145,12 +145,13 @@ def test_nondefault_scale_full():
 
 # --------------------------------------------------- the full-size workloads (sampled)
 
-def test_fwd_bf16_n4096_sampled():
-    from parity_util import sampled_check
+def test_fwd_bf16_n4096_full():
+    """The default benchmark workload (B=4, H=16, N=4096, D=128, bf16) in full: every element of
+    O, LSE, dQ, dK and dV against the oracle."""
+    from parity_util import full_check
     shape = WORKLOADS["fwd_bf16_n4096"][0]
     log("workload", shape)
-    errs, _ = sampled_check(shape, workload_seed("fwd_bf16_n4096", 0), units=[(0, 0), (1, 7), (3, 15)],
-                            n_rows=48, backward=True)
+    errs = full_check(shape, workload_seed("fwd_bf16_n4096", 0))
     log("  errors", errs)
 
 
