@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and the
 benchmark's CPU-baseline leg; never by the product path.
 """
-from .attention import (attention_backward, attention_forward, kv_head, softmax_probs,
+from .attention import (attention_backward, attention_dq_rows, attention_forward, kv_head, softmax_probs,
                         visible_mask)
 
-__all__ = ["attention_forward", "attention_backward", "kv_head", "softmax_probs", "visible_mask"]
+__all__ = ["attention_forward", "attention_backward", "attention_dq_rows", "kv_head", "softmax_probs",
+           "visible_mask"]

@@ -47,6 +47,7 @@ __all__ = [
     "softmax_probs",
     "attention_forward",
     "attention_backward",
+    "attention_dq_rows",
 ]
 
 
@@ -188,3 +189,30 @@ def attention_backward(q, k, v, do, scale: float, causal: bool, rows=None, keys=
     if return_delta:
         return dq, dk, dv, delta
     return dq, dk, dv
+
+
+def attention_dq_rows(q, k, v, do, scale: float, causal: bool, rows):
+    """dQ of the listed query rows only, float64, at a cost linear in N per row.
+
+    Row i's gradient needs nothing from other rows (same definition as attention_backward):
+      O_i, LSE_i from row i's scores,  D_i = dO_i . O_i,
+      dS_i = P_i (dO_i V^T - D_i),      dQ_i = scale * dS_i K.
+    Returns (B, Hq, len(rows), D).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Hkv, N, D = _check_shapes(q, k, v)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((B, Hq, rows.shape[0], D), dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            kv = kv_head(hq, Hq, Hkv)
+            _, P, _ = softmax_probs(q[b, hq, rows], k[b, kv], scale, rows, causal)
+            O = P @ v[b, kv]
+            delta = np.einsum("rd,rd->r", do[b, hq, rows], O)
+            dS = P * (do[b, hq, rows] @ v[b, kv].T - delta[:, None])
+            dq[b, hq] = scale * (dS @ k[b, kv])
+    return dq
+

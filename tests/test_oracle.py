@@ -14,7 +14,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import attention_backward, attention_forward, kv_head, softmax_probs, visible_mask
+from oracle import attention_backward, attention_dq_rows, attention_forward, kv_head, softmax_probs, visible_mask
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -309,26 +309,49 @@ def test_backward_constant_values():
     np.testing.assert_allclose(dv[0, 0], P0.T @ do[0, 0] + P1.T @ do[0, 1], atol=1e-13)
 
 
+@pytest.mark.parametrize("scale", [0.4, -0.3])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_torch_cpu_autograd(causal):
-    """Second, independent CPU implementation: torch float64 autograd."""
+def test_backward_torch_cpu_autograd(causal, scale):
+    """Second, independent CPU implementation: torch float64 autograd (a negative scale too)."""
     torch = pytest.importorskip("torch")
     q, k, v = qkv(B=1, Hq=4, Hkv=2, N=23, D=8, seed=71)
     do = rnd(q.shape, 72)
     tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
     kr = tk.repeat_interleave(2, dim=1); vr = tv.repeat_interleave(2, dim=1)
-    S = 0.4 * torch.matmul(tq, kr.transpose(-1, -2).contiguous())
+    S = scale * torch.matmul(tq, kr.transpose(-1, -2).contiguous())
     if causal:
         S = S.masked_fill(torch.ones(23, 23, dtype=torch.bool).triu(1), float("-inf"))
     O = torch.matmul(torch.softmax(S, dim=-1), vr)
     (O * torch.tensor(do)).sum().backward()
-    O2, L2 = attention_forward(q, k, v, 0.4, causal)
+    O2, L2 = attention_forward(q, k, v, scale, causal)
     np.testing.assert_allclose(O2, O.detach().numpy(), atol=1e-12)
     np.testing.assert_allclose(L2, torch.logsumexp(S, -1).detach().numpy(), atol=1e-12)
-    dq, dk, dv = attention_backward(q, k, v, do, 0.4, causal)
+    dq, dk, dv = attention_backward(q, k, v, do, scale, causal)
     np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+    rows = np.array([0, 5, 22])
+    np.testing.assert_allclose(attention_dq_rows(q, k, v, do, scale, causal, rows), tq.grad.numpy()[:, :, rows],
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_finite_differences(causal):
+    """attention_dq_rows against central differences of L = sum(O * dO) in the listed rows of q."""
+    q, k, v = qkv(B=1, Hq=2, Hkv=1, N=6, D=3, seed=91)
+    do = rnd(q.shape, 92)
+    rows = np.array([1, 5])
+    g = attention_dq_rows(q, k, v, do, 0.8, causal, rows)
+    h = 1e-6
+    for hq in range(2):
+        for ri, r in enumerate(rows):
+            for d in range(3):
+                qp, qm = q.copy(), q.copy()
+                qp[0, hq, r, d] += h
+                qm[0, hq, r, d] -= h
+                lp = float((attention_forward(qp, k, v, 0.8, causal)[0] * do).sum())
+                lm = float((attention_forward(qm, k, v, 0.8, causal)[0] * do).sum())
+                assert abs((lp - lm) / (2 * h) - g[0, hq, ri, d]) < 1e-7
 
 
 def test_rejects_bad_shapes():
