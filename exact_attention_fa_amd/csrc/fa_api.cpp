@@ -34,7 +34,7 @@ int check_dtype(int dtype) {
 int check_dtype16(int dtype) { return (dtype == FA_FP16 || dtype == FA_BF16) ? FA_OK : FA_ERR_DTYPE; }
 size_t elem_size(int dtype) { return dtype == FA_FP32 ? 4 : 2; }
 
-int check_scale(float s) { return (isfinite(s) && s >= 0.f) ? FA_OK : FA_ERR_SCALE; }
+int check_scale(float s) { return isfinite(s) ? FA_OK : FA_ERR_SCALE; }
 
 int check_ptr(const void* p, uintptr_t align) {
   if (p == nullptr) return FA_ERR_NULL_POINTER;
@@ -136,7 +136,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
     case FA_ERR_GQA: return "Hq must be a multiple of Hkv";
     case FA_ERR_DTYPE: return "dtype must be FA_FP16 or FA_BF16 (or FA_FP32 for fa_fwd, fa_bwd and its stages)";
-    case FA_ERR_SCALE: return "softmax_scale must be finite and >= 0";
+    case FA_ERR_SCALE: return "softmax_scale must be finite";
     case FA_ERR_ALIGNMENT: return "buffers must be 16-byte aligned (lse: 4-byte)";
     case FA_ERR_WORKSPACE: return "workspace is smaller than fa_bwd_workspace_size()";
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";

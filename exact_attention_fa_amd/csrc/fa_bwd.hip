@@ -104,7 +104,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dK,
                 uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int Hq, int Hkv,
-                int N, int n_kt, float c2, float scale, int snake, int n_qp) {
+                int N, int n_kt, float c2, float scale, uint32_t ksign, int snake, int n_qp) {
   constexpr int BKV = kBwdBKV, BQ = kBwdBQ;
   constexpr int KST = HD / 16, DB = HD / 32;
   constexpr int QT_BYTES = BQ * HD * 2;
@@ -175,14 +175,15 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (q_lo + 1 < n_qt) issue(q_lo + 1, smem + SLOT);
 
   // K and V rows of this lane's key as B operands: slot j of k-step kk = K[key][kk*16 + g*8 + j]
-  // (zero past the end: those keys' dK/dV are never stored).
+  // (zero past the end: those keys' dK/dV are never stored).  For a negative softmax scale
+  // ksign negates K, so that S c2 (c2 > 0) is still the scaled score; dK takes the signed scale.
   // They are only ever MFMA B operands and stay in AGPRs, as do the dK/dV accumulators, which
   // only MFMAs touch until the epilogue (written-out MFMAs, see fa_device.h); S and dP land in
   // VGPRs for the VALU.
   u32x4 kv[2][KST];  // [0] K, [1] V
 #pragma unroll
   for (int kk = 0; kk < KST; ++kk) {
-    kv[0][kk] = ld16_if(K + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
+    kv[0][kk] = ld16_if(K + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N) ^ ksign;
     kv[1][kk] = ld16_if(V + kvoff + (size_t)key * HD + kk * 16 + g * 8, key < N);
   }
   reg_fence(kv, true, true);
@@ -482,7 +483,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
-              int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake, int n_kp,
+              int Hq, int Hkv, int N, int n_qt, float c2, float scale, uint32_t qsign, int snake, int n_kp,
               float* __restrict__ dQp) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
   constexpr int GW = NW / SPLIT;            // waves per group
@@ -568,7 +569,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   u32x4 qf[KST], of[KST];
 #pragma unroll
   for (int kk = 0; kk < KST; ++kk) {
-    qf[kk] = ld16_if(Q + rowoff + kk * 16 + g * 8, qi < N);
+    qf[kk] = ld16_if(Q + rowoff + kk * 16 + g * 8, qi < N) ^ qsign;  // -Q for a negative scale
     of[kk] = ld16_if(dO + rowoff + kk * 16 + g * 8, qi < N);
   }
   const float l2 = qi < N ? L2[(size_t)bh * N + qi] : 0.f;
@@ -858,8 +859,15 @@ hipError_t pre_t(const BwdArgs& a) {
 }
 
 // c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
-// becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
-inline float exp2_factor(float scale) { return scale > 0.f ? scale * kLog2e : 0x1p-100f; }
+// becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).  A negative scale
+// runs as |scale| with the stationary operand of S negated (sign_bits flips the sign bit of
+// every 16-bit element): the scaled scores are unchanged, and the gradients dQ and dK are
+// multiplied by the signed scale.
+inline float exp2_factor(float scale) {
+  const float as = fabsf(scale);
+  return as > 0.f ? as * kLog2e : 0x1p-100f;
+}
+inline uint32_t sign_bits(float scale) { return scale < 0.f ? 0x80008000u : 0u; }
 
 template <typename TR, int HD, bool CAUSAL, bool PARTIAL>
 hipError_t dkdv_t(const BwdArgs& a) {
@@ -873,7 +881,8 @@ hipError_t dkdv_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), dkp, dvp, (int)a.Hq, (int)a.Hkv,
-                     (int)a.N, n_kt, exp2_factor(a.scale), a.scale, (int)grid_fits(blocks, 1), w.n_qp);
+                     (int)a.N, n_kt, exp2_factor(a.scale), a.scale, sign_bits(a.scale), (int)grid_fits(blocks, 1),
+                     w.n_qp);
   return hipGetLastError();
 }
 
@@ -897,7 +906,7 @@ hipError_t dq_nw(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dq), (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, exp2_factor(a.scale),
-                     a.scale, (int)grid_fits(blocks, 8 / NW), n_kp, dqp);
+                     a.scale, sign_bits(a.scale), (int)grid_fits(blocks, 8 / NW), n_kp, dqp);
   if constexpr (PART) {
     FA_HIP_TRY(hipGetLastError());
     const long long n8 = a.B * a.Hq * a.N * a.D / 8;

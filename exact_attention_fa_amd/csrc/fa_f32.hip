@@ -258,7 +258,9 @@ f32_bwd_dkdv_kernel(const float* __restrict__ Q, const float* __restrict__ K, co
 }
 
 // ---------------------------------------------------------------- launchers
-inline float f32_c2(float scale) { return scale > 0.f ? scale * kLog2e : 0x1p-100f; }
+// The fp32 kernels keep their running max in c2-scaled units and mask with explicit -inf, so a
+// negative scale needs no special case; a zero scale becomes 2^-100 (every exp2 rounds to 1).
+inline float f32_c2(float scale) { return scale != 0.f ? scale * kLog2e : 0x1p-100f; }
 
 template <int HD, bool CAUSAL>
 hipError_t f32_fwd_t(const FwdArgs& a) {

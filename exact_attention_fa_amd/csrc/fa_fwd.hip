@@ -61,7 +61,7 @@ template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART, int QB
 __global__ void __launch_bounds__(NW * 64, 8 / (NW * QB))
 fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
            const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-           int Hq, int Hkv, int N, int n_qt, float c2, float scale, int snake, int n_part,
+           int Hq, int Hkv, int N, int n_qt, float c2, float scale, uint32_t qsign, int snake, int n_part,
            float* __restrict__ Op, float* __restrict__ Lp) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
   static_assert(NW * QB == 4 || NW * QB == 8, "one or two workgroups per CU");
@@ -168,7 +168,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
-      qf[qb][kk] = ld16_if(Qh + (size_t)qi[qb] * HD + kk * 16 + g * 8, qi[qb] < N);
+      qf[qb][kk] = ld16_if(Qh + (size_t)qi[qb] * HD + kk * 16 + g * 8, qi[qb] < N) ^ qsign;
   if constexpr (AGPR) issue_first();
 
   // Per-lane LDS offsets.  K rows are read in the permuted order, so register i of an S^T
@@ -678,12 +678,16 @@ hipError_t launch_fwd_nw(const FwdArgs& a) {
   const int n_part = PART ? a.n_part : 1;
   const long long blocks = a.B * a.Hq * (long long)n_qt * n_part;
   // c2 must be > 0 so that exp2(-inf * c2) is an exact 0 for masked scores; a zero scale
-  // becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).
-  const float c2 = a.scale > 0.f ? a.scale * kLog2e : 0x1p-100f;
+  // becomes 2^-100, for which every exp2 rounds to exactly 1 (uniform weights).  A negative
+  // scale runs as |scale| on -Q (qsign flips the sign bit of every 16-bit element of the Q
+  // fragments): the scaled scores, and so O and LSE, are unchanged.
+  const float as = fabsf(a.scale);
+  const float c2 = as > 0.f ? as * kLog2e : 0x1p-100f;
+  const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   hipLaunchKernelGGL((fwd_kernel<TR, HD, CAUSAL, NW, SPLIT, PART, QB>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, a.scale, (int)grid_fits(blocks, 8 / (NW * QB)), n_part,
+                     (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, c2, as, qsign, (int)grid_fits(blocks, 8 / (NW * QB)), n_part,
                      a.o_part, a.lse_part);
   return hipGetLastError();
 }

@@ -35,7 +35,8 @@
  *              (MHA, GQA and MQA).
  *   Causal     causal != 0: key j is visible to query i iff j <= i (square, top-left).
  *              Blocks above the diagonal are skipped, not computed and masked.
- *   Scale      softmax_scale must be finite and >= 0 (0 gives uniform attention).
+ *   Scale      softmax_scale: any finite value.  0 gives uniform attention; a negative scale
+ *              is exact too (the kernels run |scale| on the negated Q, or K, operand).
  *   D          64 or 128.  N >= 1, arbitrary (ragged tails need no padding).
  *   Pointers   device pointers, 16-byte aligned, not aliasing one another.  The caller
  *              owns every buffer; inputs are only read, outputs are fully overwritten.
@@ -73,7 +74,7 @@ enum fa_status {
   FA_ERR_HEAD_DIM = 3,     /* D is not 64 or 128 */
   FA_ERR_GQA = 4,          /* Hq is not a multiple of Hkv */
   FA_ERR_DTYPE = 5,        /* dtype is not FA_FP16 / FA_BF16 (/ FA_FP32 where accepted) */
-  FA_ERR_SCALE = 6,        /* softmax_scale is negative, NaN or infinite */
+  FA_ERR_SCALE = 6,        /* softmax_scale is NaN or infinite */
   FA_ERR_ALIGNMENT = 7,    /* a pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = 8,    /* workspace_bytes < fa_bwd_workspace_size(...) */
   FA_ERR_HIP = 9,          /* the HIP runtime rejected a launch */

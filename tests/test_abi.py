@@ -86,7 +86,10 @@ def fwd(lib, q=0, k=1, v=2, o=3, l=4, B=1, Hq=2, Hkv=2, N=256, D=64, scale=0.125
     (dict(Hq=6, Hkv=4), "FA_ERR_GQA"),
     (dict(scale=float("nan")), "FA_ERR_SCALE"),
     (dict(scale=float("inf")), "FA_ERR_SCALE"),
-    (dict(scale=-0.5), "FA_ERR_SCALE"),
+    # a finite negative scale passes validation: the call fails later, at the null pointer
+    (dict(scale=-0.5, q=ctypes.c_void_p(0)), "FA_ERR_NULL_POINTER"),
+    (dict(scale=-1e30, q=ctypes.c_void_p(0)), "FA_ERR_NULL_POINTER"),
+    (dict(scale=float("-inf")), "FA_ERR_SCALE"),
     (dict(N=1 << 26, D=128), "FA_ERR_TOO_LARGE"),
     (dict(B=1 << 20, Hq=1 << 12, Hkv=1 << 12), "FA_ERR_TOO_LARGE"),
     (dict(q=ctypes.c_void_p(0)), "FA_ERR_NULL_POINTER"),
@@ -137,7 +140,8 @@ def test_bwd_rejects(lib):
     assert bwd(lib, ws_bytes=need - 1) == STATUS["FA_ERR_WORKSPACE"]
     assert bwd(lib, D=80) == STATUS["FA_ERR_HEAD_DIM"]
     assert bwd(lib, dtype=7) == STATUS["FA_ERR_DTYPE"]
-    assert bwd(lib, scale=-1.0) == STATUS["FA_ERR_SCALE"]
+    assert bwd(lib, scale=float("nan")) == STATUS["FA_ERR_SCALE"]
+    assert bwd(lib, scale=-1.0, dq=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]  # accepted scale
     assert bwd(lib, dq=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]
     assert bwd(lib, dv=ctypes.c_void_p(A + 4)) == STATUS["FA_ERR_ALIGNMENT"]
     assert bwd(lib, dq=ptr(0)) == STATUS["FA_ERR_ALIAS"]
@@ -164,8 +168,11 @@ def test_stage_entry_points_reject(lib):
                          None) == STATUS["FA_ERR_NULL_POINTER"]
     assert lib.fa_bwd_dq(ptr(0), ptr(1), ptr(2), ptr(3), ptr(0), ptr(5), need, B, Hq, Hkv, N, D, 0.1, 1, 1,
                          None) == STATUS["FA_ERR_ALIAS"]
-    assert lib.fa_bwd_dq(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), need, B, Hq, Hkv, N, D, -0.1, 1, 1,
-                         None) == STATUS["FA_ERR_SCALE"]
+    assert lib.fa_bwd_dq(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), need, B, Hq, Hkv, N, D,
+                         float("inf"), 1, 1, None) == STATUS["FA_ERR_SCALE"]
+    # a negative scale is accepted: the call fails later, at the aliased output
+    assert lib.fa_bwd_dq(ptr(0), ptr(1), ptr(2), ptr(3), ptr(0), ptr(5), need, B, Hq, Hkv, N, D, -0.1, 1, 1,
+                         None) == STATUS["FA_ERR_ALIAS"]
     assert lib.fa_bwd_postprocess(None, ptr(2), ptr(5), need, B, Hq, Hkv, N, D, 1, None) == \
         STATUS["FA_ERR_NULL_POINTER"]
     assert lib.fa_bwd_postprocess(ptr(1), ptr(2), ptr(1), need, B, Hq, Hkv, N, D, 1, None) == \

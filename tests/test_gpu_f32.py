@@ -70,6 +70,24 @@ def test_f32_full(dims):
     log("  errors", eo, el, errs)
 
 
+def test_f32_negative_scale():
+    """The fp32 path keeps its running max in scaled units, so a negative scale is exact too."""
+    import torch
+    import exact_attention_fa_amd as fa
+    from parity_util import attention_backward, attention_forward, f64
+    shape = Shape(1, 4, 2, 300, 64, "fp32", True)
+    q, k, v, do = make_inputs(shape, seed=4242)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=True, softmax_scale=-0.2)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, dod, lse, causal=True, softmax_scale=-0.2)
+    torch.cuda.synchronize()
+    o_r, l_r = attention_forward(f64(q), f64(k), f64(v), -0.2, True)
+    assert float(np.abs(f64(o) - o_r).max()) <= TOL_O32 and float(np.abs(f64(lse) - l_r).max()) <= TOL_LSE32
+    for g, r in zip((dq, dk, dv), attention_backward(f64(q), f64(k), f64(v), f64(do), -0.2, True)):
+        assert float(np.abs(f64(g) - r).max() / max(np.abs(r).max(), 1e-2)) <= TOL_GRAD32
+
+
 def test_f32_checks_the_16bit_path():
     """Gradient checking: the fp32 path on the bf16 inputs (upcast) against the bf16 kernels;
     the difference stays within the 16-bit tolerances."""

@@ -125,7 +125,7 @@ def test_rejected_call_writes_nothing(torch_fa):
     o = torch.full_like(q, 7.0)
     lse = torch.full((1, 2, 100), 3.0, device="cuda")
     with pytest.raises(RuntimeError, match="softmax_scale"):
-        fa.fa_fwd(q, q, q, softmax_scale=-1.0, out=o, lse=lse)
+        fa.fa_fwd(q, q, q, softmax_scale=float("nan"), out=o, lse=lse)
     with pytest.raises(RuntimeError, match="head dim"):
         x = torch.randn(1, 2, 100, 96, device="cuda").half()
         fa.fa_fwd(x, x, x)
