@@ -114,24 +114,38 @@ def _dtype_code(t):
 
 
 def _dims(q, k, v):
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise RuntimeError("q, k, v must be 4-D (B, H, N, D)")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None or t.dim() != 4:
+            raise RuntimeError(f"{name} must be a 4-D tensor (B, H, N, D)")
     B, Hq, N, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
         raise RuntimeError("k and v must be (B, Hkv, N, D) with the B, N, D of q")
     return B, Hq, k.shape[1], N, D
 
 
-def _require(*tensors, dtype=None):
-    for t in tensors:
+def _validate(*specs):
+    """Checks tensor arguments before anything reaches the library: first the shape and dtype
+    of every one, then device and contiguity.  The C ABI sees only pointers, so a wrongly
+    shaped, typed, strided or host tensor would otherwise be read or written out of bounds.
+    Each spec is (tensor, name, shape or None, numel or None, dtype or None); all tensors must
+    share the first one's device."""
+    for t, name, shape, numel, dtype in specs:
         if t is None:
-            continue
-        if not t.is_cuda:
-            raise RuntimeError("tensors must live on the GPU")
-        if not t.is_contiguous():
-            raise RuntimeError("tensors must be contiguous")
+            raise RuntimeError(f"{name} is required")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise RuntimeError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if numel is not None and t.numel() != numel:
+            raise RuntimeError(f"{name} has {t.numel()} elements, expected {numel}")
         if dtype is not None and t.dtype != dtype:
-            raise RuntimeError(f"dtype mismatch: expected {dtype}, got {t.dtype}")
+            raise RuntimeError(f"{name}: dtype mismatch, expected {dtype}, got {t.dtype}")
+    device = specs[0][0].device
+    for t, name, *_ in specs:
+        if not t.is_cuda:
+            raise RuntimeError(f"{name} must live on the GPU")
+        if t.device != device:
+            raise RuntimeError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise RuntimeError(f"{name} must be contiguous")
 
 
 def _stream(t):
@@ -151,16 +165,18 @@ def _scale(D, softmax_scale):
     return 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
 
 
+def _qkv_specs(q, k, v):
+    return [(q, "q", None, None, q.dtype), (k, "k", None, None, q.dtype), (v, "v", None, None, q.dtype)]
+
+
 def fa_fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
     """Forward: returns (o, lse); o like q, lse float32 (B, Hq, N) in natural-log units."""
     import torch
     B, Hq, Hkv, N, D = _dims(q, k, v)
-    _require(q, k, v, dtype=q.dtype)
     code = _dtype_code(q)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _require(o, dtype=q.dtype)
-    _require(l, dtype=torch.float32)
+    _validate(*_qkv_specs(q, k, v), (o, "out", q.shape, None, q.dtype), (l, "lse", (B, Hq, N), None, torch.float32))
     rc = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, Hq, Hkv, N, D,
                                _scale(D, softmax_scale), int(bool(causal)), code, _stream(q))
     _check(rc, "fa_fwd")
@@ -182,16 +198,16 @@ def fa_fwd_splitkv(q, k, v, causal: bool = False, softmax_scale=None, n_split: i
     choice); returns (o, lse) like fa_fwd."""
     import torch
     B, Hq, Hkv, N, D = _dims(q, k, v)
-    _require(q, k, v, dtype=q.dtype)
     code = _dtype_code(q)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _require(o, dtype=q.dtype)
-    _require(l, dtype=torch.float32)
+    _validate(*_qkv_specs(q, k, v), (o, "out", q.shape, None, q.dtype), (l, "lse", (B, Hq, N), None, torch.float32))
     n = fa_fwd_splitkv_parts(B, Hq, Hkv, N, D, causal) if n_split == 0 else int(n_split)
     if workspace is None and 1 <= n <= 64:
         need = fa_fwd_splitkv_workspace_size(B, Hq, Hkv, N, D, n)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    if workspace is not None:
+        _validate((q, "q", None, None, None), (workspace, "workspace", None, None, None))
     nbytes = 0 if workspace is None else _nbytes(workspace)
     rc = load_library().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(workspace), nbytes,
                                        int(n_split), B, Hq, Hkv, N, D, _scale(D, softmax_scale),
@@ -205,12 +221,15 @@ def fa_merge_partials(o_parts, lse_parts, out, lse):
     (n, rows) -> out (rows, D) in out's dtype, lse (rows,) float32 (any shapes with these
     element counts)."""
     import torch
+    if lse_parts.dim() < 1 or lse_parts.numel() == 0:
+        raise RuntimeError("lse_parts must be (n_parts, rows)")
     n = lse_parts.shape[0]
     rows = lse_parts.numel() // n
+    if o_parts.numel() % (n * rows) != 0:
+        raise RuntimeError("o_parts must hold n_parts * rows * D elements")
     D = o_parts.numel() // (n * rows)
-    _require(o_parts, lse_parts, dtype=torch.float32)
-    _require(out)
-    _require(lse, dtype=torch.float32)
+    _validate((o_parts, "o_parts", None, None, torch.float32), (lse_parts, "lse_parts", None, n * rows, torch.float32),
+              (out, "out", None, rows * D, None), (lse, "lse", None, rows, torch.float32))
     rc = load_library().fa_merge_partials(_ptr(o_parts), _ptr(lse_parts), n, _ptr(out), _ptr(lse), rows, D,
                                           _dtype_code(out), _stream(out))
     _check(rc, "fa_merge_partials")
@@ -233,13 +252,16 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale=None, worksp
     """Backward: returns (dq, dk, dv) in the dtype of q."""
     import torch
     B, Hq, Hkv, N, D = _dims(q, k, v)
-    _require(q, k, v, o, do, dtype=q.dtype)
-    _require(lse, dtype=torch.float32)
     code = _dtype_code(q)
+    specs = [*_qkv_specs(q, k, v), (o, "o", q.shape, None, q.dtype), (do, "do", q.shape, None, q.dtype),
+             (lse, "lse", (B, Hq, N), None, torch.float32)]
+    for t, name, shape in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape), (workspace, "workspace", None)):
+        if t is not None:
+            specs.append((t, name, shape, None, None if name == "workspace" else q.dtype))
+    _validate(*specs)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _require(dq, dk, dv, dtype=q.dtype)
     ws, nbytes = _workspace(q, (B, Hq, Hkv, N, D), workspace)
     rc = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                _ptr(dk), _ptr(dv), _ptr(ws), nbytes, B, Hq, Hkv, N, D,
@@ -249,8 +271,13 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale=None, worksp
 
 
 def fa_bwd_preprocess(o, do, lse, workspace, Hkv: int):
+    import torch
+    if o is None or o.dim() != 4:
+        raise RuntimeError("o must be a 4-D tensor (B, Hq, N, D)")
     B, Hq, N, D = o.shape
-    _require(o, do, dtype=o.dtype)
+    _dtype_code(o)
+    _validate((o, "o", None, None, o.dtype), (do, "do", o.shape, None, o.dtype),
+              (lse, "lse", (B, Hq, N), None, torch.float32), (workspace, "workspace", None, None, None))
     rc = load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(),
                                           B, Hq, Hkv, N, D, _dtype_code(o), _stream(o))
@@ -258,7 +285,13 @@ def fa_bwd_preprocess(o, do, lse, workspace, Hkv: int):
 
 
 def fa_bwd_dkdv(q, k, v, do, dk, dv, workspace, causal=False, softmax_scale=None):
+    """dk/dv may be None where the pass writes partials into the workspace (Hq > Hkv, or
+    query-range pieces); the library then does not touch them."""
     B, Hq, Hkv, N, D = _dims(q, k, v)
+    _dtype_code(q)
+    specs = [*_qkv_specs(q, k, v), (do, "do", q.shape, None, q.dtype), (workspace, "workspace", None, None, None)]
+    specs += [(x, name, k.shape, None, q.dtype) for x, name in ((dk, "dk"), (dv, "dv")) if x is not None]
+    _validate(*specs)
     rc = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
                                     _ptr(workspace), _nbytes(workspace), B, Hq, Hkv, N, D,
                                     _scale(D, softmax_scale), int(bool(causal)), _dtype_code(q),
@@ -268,6 +301,9 @@ def fa_bwd_dkdv(q, k, v, do, dk, dv, workspace, causal=False, softmax_scale=None
 
 def fa_bwd_dq(q, k, v, do, dq, workspace, causal=False, softmax_scale=None):
     B, Hq, Hkv, N, D = _dims(q, k, v)
+    _dtype_code(q)
+    _validate(*_qkv_specs(q, k, v), (do, "do", q.shape, None, q.dtype), (dq, "dq", q.shape, None, q.dtype),
+              (workspace, "workspace", None, None, None))
     rc = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(workspace),
                                   _nbytes(workspace), B, Hq, Hkv, N, D, _scale(D, softmax_scale),
                                   int(bool(causal)), _dtype_code(q), _stream(q))
@@ -275,7 +311,12 @@ def fa_bwd_dq(q, k, v, do, dq, workspace, causal=False, softmax_scale=None):
 
 
 def fa_bwd_postprocess(dk, dv, workspace, Hq: int):
+    if dk is None or dk.dim() != 4:
+        raise RuntimeError("dk must be a 4-D tensor (B, Hkv, N, D)")
     B, Hkv, N, D = dk.shape
+    _dtype_code(dk)
+    _validate((dk, "dk", None, None, dk.dtype), (dv, "dv", dk.shape, None, dk.dtype),
+              (workspace, "workspace", None, None, None))
     rc = load_library().fa_bwd_postprocess(_ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace),
                                            B, Hq, Hkv, N, D, _dtype_code(dk), _stream(dk))
     _check(rc, "fa_bwd_postprocess")
