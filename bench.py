@@ -18,7 +18,21 @@ Prints ONE JSON line on stdout:
                   launch over its HIP-event time, against the HBM peak
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
   kernel_*_ms     per-kernel average, median, minimum and maximum over the timed steps
-  gpu_clock       the shader clock rocm-smi reports before the warmup and after the timed steps
+  mfma_util       MFMA busy fraction and sustained shader clock of the dominant kernel, from
+                  the committed hardware-counter summary under profiles/ (null when the
+                  kernel source has changed since the counters were taken)
+  gpu_clock       the shader clock level the driver reports (sysfs, read in-process) before
+                  the warmup and after the timed steps
+
+`value` and `ms_per_step` use the median of the per-step HIP-event durations (the pages'
+protocol: warmups, then the median of the timed repetitions); `wall_ms_per_step` is the
+host wall time of the whole timed region divided by the steps.  The default workload is the
+long non-causal bf16 sequence (B=1, H=16, N=16384, D=128).  The tiny fp16 workloads
+(`--workload tiny_fp16_nc` / `tiny_fp16_causal`, B=1, H=2, N=256, D=64) are latency-bound:
+their line adds microseconds per kernel and the step's algorithmic HBM bytes per second.
+
+The script starts no child process: under a profiler every child would inherit the
+profiler's preloaded library.
 
 FLOP convention: forward 4*B*H*N^2*D, backward 10*B*H*N^2*D (five N x N x D products,
 including the recompute of S), halved when causal.
@@ -27,6 +41,8 @@ including the recompute of S), halved when causal.
 times (the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
 `--ceilings` instead measures what the GPU sustains on plain library work (8192^3 bf16 and
 fp16 GEMMs, 2 GiB HBM read and copy), context for the roofline fractions, and exits.
+`--summarize KIND DIR...` reads rocprofv3 CSV output (no GPU) and prints the summary lines that
+the files under profiles/ hold (see summarize()).
 """
 from __future__ import annotations
 
@@ -37,7 +53,6 @@ import os
 import platform
 import re
 import statistics
-import subprocess
 import sys
 import time
 
@@ -49,6 +64,8 @@ PEAK_MFMA_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16/fp16 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
 WORKLOAD_KEYS = {
+    "tiny_fp16_nc": ("tiny_fp16", 0),
+    "tiny_fp16_causal": ("tiny_fp16", 1),
     "fwd_bf16_n4096": ("fwd_bf16_n4096", 0),
     "fwd_bf16_n8192": ("fwd_bf16_long", 0),
     "fwd_bf16_n16384": ("fwd_bf16_long", 1),
@@ -145,16 +162,23 @@ def machine_ceilings():
 
 
 def gpu_clock():
-    """The shader clock as rocm-smi reports it (a read-only query, outside any timed region),
-    or None where the tool is missing or its output cannot be read."""
+    """The shader clock levels the amdgpu driver lists in sysfs (the current one is marked
+    with '*'), read as plain files in this process, or None where they cannot be read.  Each
+    card visible in sysfs is reported by its PCI address."""
+    out = {}
     try:
-        r = subprocess.run([os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "rocm-smi"), "-g", "--json"],
-                           capture_output=True, text=True, timeout=15)
-        d = json.loads(r.stdout[r.stdout.index("{"):])
-        card = d[sorted(d)[0]]
-        return {k.strip(" :"): v for k, v in card.items() if "sclk" in k.lower()} or None
-    except Exception:  # the clock is context for the numbers, never a reason to fail the run
+        for card in sorted(os.listdir("/sys/class/drm")):
+            path = os.path.join("/sys/class/drm", card, "device", "pp_dpm_sclk")
+            if not card.startswith("card") or "-" in card or not os.path.exists(path):
+                continue
+            with open(path) as f:
+                cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+            pci = os.path.basename(os.path.realpath(os.path.join("/sys/class/drm", card, "device")))
+            if cur:
+                out[pci] = cur[0].rstrip(" *")
+    except OSError:  # the clock is context for the numbers, never a reason to fail the run
         return None
+    return out or None
 
 
 def copy_calibration(nbytes):
@@ -216,17 +240,137 @@ def cpu_baseline(shape, seed, budget_s):
     }
 
 
+def algorithmic_bytes(shape):
+    """Algorithmic HBM bytes of each timed stage: every input read once and every output
+    written once (K/V re-reads across query tiles and Q/dO re-reads across key blocks are
+    implementation traffic, not counted)."""
+    es = 2 if shape.dtype in ("bf16", "fp16") else 4
+    q = shape.B * shape.Hq * shape.N * shape.D * es
+    kv = shape.B * shape.Hkv * shape.N * shape.D * es
+    rows = shape.B * shape.Hq * shape.N
+    return {
+        "fwd": 2 * q + 2 * kv + 4 * rows,                    # Q, K, V read; O, LSE written
+        "bwd_preprocess": 2 * q + 4 * rows + 8 * rows,       # O, dO, LSE read; -D, LSE*log2 e written
+        "bwd_dkdv": 2 * q + 2 * kv + 8 * rows + 2 * kv,      # Q, dO, K, V, LSE, D read; dK, dV written
+        "bwd_dq": 2 * q + 2 * kv + 8 * rows + q,             # Q, dO, K, V, LSE, D read; dQ written
+        "bwd_postprocess": 0,                                # partials only (none for MHA grids)
+    }
+
+
+def counter_summary(kernel, workload):
+    """MFMA busy fraction and sustained shader clock from profiles/busy_<kernel>_<workload>.txt,
+    if that summary was taken on the current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"busy_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.split("#", 1)[0].strip()
+    if kv.get("source_sha256_16") != source_hash(kernel):
+        return None
+    try:
+        return {"kernel": kernel, "mfma_busy_frac": float(kv["mfma_busy_frac"]),
+                "sclk_mhz_sustained": float(kv["sclk_mhz_sustained"]),
+                "source": f"profiles/busy_{kernel}_{workload}.txt"}
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+
+def _csv_rows(directory, suffix):
+    import csv
+    rows = []
+    for base, _, files in os.walk(directory):
+        for name in sorted(files):
+            if name.endswith(suffix):
+                with open(os.path.join(base, name), newline="") as f:
+                    rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def _short(name):
+    """Kernel name without namespaces, return type and argument list."""
+    name = name.replace("(anonymous namespace)::", "").replace("fa::", "")
+    name = re.sub(r"^void ", "", name)
+    depth = 0
+    for i, ch in enumerate(name):  # cut at the argument list: the first '(' outside <...>
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def summarize(kind, dirs, skip=0):
+    """Summary lines from rocprofv3 CSV output, per kernel (the template name shortened):
+      trace DIR       average dispatch duration (us) over the dispatches after the first `skip`
+      counters DIR..  per-dispatch averages of every collected counter (one or more runs)
+      busy DIR..      from SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE and the dispatches' own
+                      timestamps: MFMA busy fraction per SIMD (busy cycles / 1024 SIMDs / the
+                      kernel's cycles) and the sustained shader clock (GRBM_GUI_ACTIVE / 8 XCDs /
+                      duration)
+    Prints `kernel: key = value` lines; no GPU is needed."""
+    from collections import defaultdict
+    if kind == "trace":
+        rows = _csv_rows(dirs[0], "kernel_trace.csv")
+        dur = defaultdict(list)
+        for r in rows:
+            dur[_short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for k, v in dur.items():
+            v = v[skip:] or v
+            print(f"{k}: dispatches = {len(v)}; avg_us = {statistics.fmean(v):.1f}; "
+                  f"median_us = {statistics.median(v):.1f}; min_us = {min(v):.1f}; max_us = {max(v):.1f}")
+        return
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = _short(r["Kernel_Name"])
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if "Start_Timestamp" in r and "End_Timestamp" in r:
+                durs[k][(d, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    for k, cs in vals.items():
+        avg = {c: statistics.fmean(v) for c, v in cs.items()}
+        dur_us = statistics.fmean(durs[k].values()) if durs[k] else None
+        if kind == "counters":
+            print(f"{k}: " + "; ".join(f"{c} = {v:.4g}" for c, v in sorted(avg.items())))
+            continue
+        gui = avg.get("GRBM_GUI_ACTIVE")
+        mfma = avg.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if gui is None or mfma is None:
+            continue
+        cycles = gui / 8.0                       # per XCD: the kernel's duration in shader cycles
+        busy = mfma / 1024.0 / cycles            # 1024 SIMDs (256 CUs x 4)
+        line = f"{k}: mfma_busy_frac = {busy:.4f}; gui_cycles_per_xcd = {cycles:.4g}"
+        if dur_us:
+            line += f"; dur_us = {dur_us:.1f}; sclk_mhz_sustained = {cycles / dur_us:.0f}"
+        print(line)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwd_bf16_n4096", choices=sorted(WORKLOAD_KEYS))
+    ap.add_argument("--workload", default="fwd_bf16_n16384", choices=sorted(WORKLOAD_KEYS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--ceilings", action="store_true", help="measure library GEMM and HBM rates and exit")
+    ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
+                    help="summarise rocprofv3 CSV output: trace DIR | counters DIR... | busy DIR...")
+    ap.add_argument("--skip", type=int, default=0, help="with --summarize trace: dispatches to skip")
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize[0], args.summarize[1:], args.skip)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (attention heads and "
@@ -307,11 +451,12 @@ def main():
         step_ms.append(ev[0].elapsed_time(ev[len(kernels)]))
     avg = {kname: statistics.fmean(vals) for kname, vals in per_kernel.items()}
     med = {kname: statistics.median(vals) for kname, vals in per_kernel.items()}
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = statistics.median(step_ms)
 
     f_fwd, f_bwd = flops(shape, True, False), flops(shape, False, True)
-    fwd_ms = avg["fwd"]
-    bwd_ms = sum(avg[kname] for kname in kernels if kname != "fwd")
+    fwd_ms = med["fwd"]
+    bwd_ms = statistics.median([sum(per_kernel[kname][s] for kname in kernels if kname != "fwd")
+                                for s in range(args.steps)])
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     dominant = max(kernels, key=lambda kname: avg[kname])
     # Algorithmic FLOPs per launch: the dK/dV pass does four of the backward's five N x N x D
@@ -319,17 +464,23 @@ def main():
     # (another 0.4 of the backward's FLOPs) is work this design adds, so it is not credited.
     kflops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.2 * f_bwd,
               "bwd_preprocess": 0.0, "bwd_postprocess": 0.0}
-    if kflops[dominant] > 0:
+    kbytes = algorithmic_bytes(shape)
+    latency_bound = name == "tiny_fp16"
+    if latency_bound:
+        # A few hundred kilobytes per launch: every kernel is bound by launch and memory latency,
+        # and the HBM rate of its algorithmic bytes is reported against the HBM peak.
+        gbs = kbytes[dominant] / (avg[dominant] * 1e-3) / 1e9
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 5), "traffic": None,
+                    "avg_ms": round(avg[dominant], 4), "note": "latency-bound launch"}
+    else:
         achieved = kflops[dominant] / (avg[dominant] * 1e-3) / 1e12
         roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                     "traffic": measured_traffic(dominant, args.workload), "avg_ms": round(avg[dominant], 4)}
-    else:  # pragma: no cover - the contractions dominate every listed workload
-        roofline = None
     # The memory-bound stage: the preprocess reads O and dO (input dtype) and the LSE, and
     # writes -D and LSE*log2(e), all fp32 per row.
-    rows = B * Hq * N
-    pre_bytes = rows * (2 * D * (2 if shape.dtype in ("bf16", "fp16") else 4) + 4 + 8)
+    pre_bytes = kbytes["bwd_preprocess"]
     pre_gbs = pre_bytes / (avg["bwd_preprocess"] * 1e-3) / 1e9
     hbm = {"kernel": "bwd_preprocess", "bound": "hbm", "achieved": round(pre_gbs, 1), "peak": PEAK_HBM_GBS,
            "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": pre_bytes,
@@ -351,6 +502,7 @@ def main():
         "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D,
                    "causal": causal, "softmax_scale": scale, "inputs": "N(0,1) seeded, cast RNE"
                    + (f", x{shape.mult}" if shape.mult != 1.0 else ""), "fwd_key_pieces": n_split},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
         "fwd_pct_peak": round(100 * f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 2),
@@ -360,10 +512,20 @@ def main():
         "kernel_min_ms": {kname: round(min(vals), 4) for kname, vals in per_kernel.items()},
         "kernel_max_ms": {kname: round(max(vals), 4) for kname, vals in per_kernel.items()},
         "gpu_clock": {"before": clock_before, "after": clock_after},
+        "mfma_util": None if latency_bound else counter_summary(dominant, args.workload),
         "roofline": roofline,
         "hbm": hbm,
         "cpu_baseline": None,
     }
+    if latency_bound:
+        step_bytes = sum(kbytes.values())
+        out["latency"] = {
+            "step_us": round(ms_per_step * 1e3, 2),
+            "kernel_median_us": {kname: round(val * 1e3, 2) for kname, val in med.items()},
+            "step_algorithmic_bytes": step_bytes,
+            "step_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+            "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, seed, args.cpu_budget)
     print(json.dumps(out), flush=True)
