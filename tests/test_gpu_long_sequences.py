@@ -1,9 +1,9 @@
 """Sequences far longer than the benchmarked ones (N = 131072 and 65536): head offsets, tile
 counts and grid sizes well away from the small cases.
 
-The forward is compared with the oracle on sampled rows (a row's O and LSE need only that
-row's scores).  The backward's full oracle needs every row's statistics, which is too slow at
-this length, so it is checked through properties that hold at any size:
+The forward, and the backward's dQ, are compared with the oracle on sampled rows (a row's O,
+LSE and dQ need only that row's scores).  dK and dV need every row's statistics, too slow for
+the oracle at this length, so they are checked through properties that hold at any size:
   * every row of dS sums to zero, so sum_j dK_j = 0;
   * every row of P sums to one, so sum_j dV_j = sum over the group's query heads of sum_i dO_i;
   * causal: only the last query sees the last key, so dV_{N-1} and dK_{N-1} are single terms,
@@ -43,7 +43,7 @@ def test_long_sequence(dims):
     import exact_attention_fa_amd as fa
     from exact_attention_fa_amd.inputs import Shape, make_inputs
     from parity_util import TOL_GRAD, assert_fwd_close, f64
-    from oracle import attention_forward
+    from oracle import attention_dq_rows, attention_forward
 
     B, Hq, Hkv, N, D, dtype, causal = dims
     shape = Shape(B, Hq, Hkv, N, D, dtype, causal)
@@ -63,6 +63,12 @@ def test_long_sequence(dims):
     o_ref, lse_ref = attention_forward(qh, kh, vh, scale, causal, rows=rows)
     eo, el = assert_fwd_close(f64(o)[:, :, rows], f64(lse)[:, :, rows], o_ref, lse_ref, str(shape))
     log("  forward sampled rows: O err %.2e, LSE err %.2e" % (eo, el))
+
+    # backward, dQ of the sampled rows: a row's gradient needs only that row's statistics
+    dq_ref = attention_dq_rows(qh, kh, vh, f64(do), scale, causal, rows)
+    e_dq = float(np.abs(f64(dq)[:, :, rows] - dq_ref).max() / max(np.abs(dq_ref).max(), 1e-2))
+    log("  dQ sampled rows relative error %.2e" % e_dq)
+    assert e_dq <= TOL_GRAD, f"{shape}: sampled dQ rows relative error {e_dq:.3e}"
 
     # backward: sum_j dK_j = 0 and sum_j dV_j = sum_group sum_i dO_i, per KV head and column
     dk64, dv64, do64 = dk.double(), dv.double(), do.double()

@@ -1,5 +1,5 @@
-"""The torch.library registration: shape propagation without a GPU, and on the GPU autograd
-and torch.compile against the direct C-ABI calls."""
+"""The torch.library registration: shape propagation without a GPU; on the GPU, autograd
+against the CPU oracle and the direct C-ABI calls, and torch.compile without a graph break."""
 import pytest
 import torch
 
@@ -27,19 +27,33 @@ def test_op_refuses_cpu_tensors():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("causal", [False, True])
-def test_autograd_matches_direct_calls(causal):
+def test_autograd_matches_oracle_and_direct_calls(causal):
+    """Forward and autograd backward of the registered op against the CPU oracle (the parity
+    tolerances), and bit for bit against the direct C-ABI calls it wraps."""
     import exact_attention_fa_amd as fa
     from exact_attention_fa_amd.torch_op import attention
     from exact_attention_fa_amd.inputs import Shape, make_inputs
+    from parity_util import TOL_O, assert_fwd_close, assert_grad_close, f64
+    from oracle import attention_backward, attention_forward
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible")
-    q, k, v, do = (t.cuda() for t in make_inputs(Shape(2, 8, 2, 300, 128, "bf16", causal), 31))
+    shape = Shape(2, 8, 2, 300, 128, "bf16", causal)
+    qc, kc, vc, doc = make_inputs(shape, 31)
+    q, k, v, do = (t.cuda() for t in (qc, kc, vc, doc))
     qr, kr, vr = (t.clone().requires_grad_(True) for t in (q, k, v))
     o = attention(qr, kr, vr, causal=causal)
     o.backward(do)
+    torch.cuda.synchronize()
+    o_r, l_r = attention_forward(f64(qc), f64(kc), f64(vc), shape.scale, causal)
+    eo = float(abs(f64(o) - o_r).max())  # the op returns O only; its LSE is checked below via fa_fwd
+    assert eo <= TOL_O, f"torch op: O max-abs error {eo:.3e}"
+    refs = attention_backward(f64(qc), f64(kc), f64(vc), f64(doc), shape.scale, causal)
+    for name, g, r in zip(("dq", "dk", "dv"), (qr.grad, kr.grad, vr.grad), refs):
+        assert_grad_close(f64(g), r, name, "torch op")
     o2, lse2 = fa.fa_fwd(q, k, v, causal=causal)
     dq2, dk2, dv2 = fa.fa_bwd(q, k, v, o2, do, lse2, causal=causal)
     torch.cuda.synchronize()
+    assert_fwd_close(f64(o2), f64(lse2), o_r, l_r, "fa_fwd under the op")
     assert torch.equal(o.detach(), o2)
     assert torch.equal(qr.grad, dq2) and torch.equal(kr.grad, dk2) and torch.equal(vr.grad, dv2)
 
