@@ -25,7 +25,7 @@ __all__ = [
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_size",
     "fa_merge_partials", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_postprocess",
     "fa_bwd_workspace_size", "fa_version", "fa_status_string", "library_path", "load_library",
-    "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16", "FA_FP32",
+    "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16", "FA_FP32", "fa_bwd_noalloc", "FA_NOALLOC_SCRATCH_BYTES",
 ]
 
 FA_FP16 = 0
@@ -62,7 +62,11 @@ _SIGS = {
                   ctypes.c_int),
     "fa_bwd_postprocess": ([_vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
                             ctypes.c_int, _vp], ctypes.c_int),
+    "fa_bwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                        _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
+                       ctypes.c_int),
 }
+FA_NOALLOC_SCRATCH_BYTES = 80 * 1024 * 1024  # the library's static backward workspace per GPU
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
 
@@ -267,6 +271,27 @@ def fa_bwd(q, k, v, o, do, lse, causal: bool = False, softmax_scale=None, worksp
                                _ptr(dk), _ptr(dv), _ptr(ws), nbytes, B, Hq, Hkv, N, D,
                                _scale(D, softmax_scale), int(bool(causal)), code, _stream(q))
     _check(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, causal: bool = False, softmax_scale=None, dq=None, dk=None, dv=None):
+    """fa_bwd with the library's static scratch as workspace (the C entry point allocates
+    nothing; outputs not given are allocated here by torch).  Returns (dq, dk, dv)."""
+    import torch
+    B, Hq, Hkv, N, D = _dims(q, k, v)
+    code = _dtype_code(q)
+    specs = [*_qkv_specs(q, k, v), (o, "o", q.shape, None, q.dtype), (do, "do", q.shape, None, q.dtype),
+             (lse, "lse", (B, Hq, N), None, torch.float32)]
+    specs += [(t, name, shape, None, q.dtype) for t, name, shape in ((dq, "dq", q.shape), (dk, "dk", k.shape),
+                                                                     (dv, "dv", k.shape)) if t is not None]
+    _validate(*specs)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    rc = load_library().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, Hq, Hkv, N, D, _scale(D, softmax_scale),
+                                       int(bool(causal)), code, _stream(q))
+    _check(rc, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -143,6 +143,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_TOO_LARGE: return "problem size exceeds the 32-bit index range of the kernels";
     case FA_ERR_ALIAS: return "an output buffer overlaps another buffer of the call";
     case FA_ERR_SPLIT: return "split / part count out of range (1..64, or 0 for the library's choice)";
+    case FA_ERR_SCRATCH: return "fa_bwd_noalloc: the call needs more workspace than the 80 MiB static scratch";
     default: return "unknown status";
   }
 }

@@ -42,7 +42,8 @@
  *              owns every buffer; inputs are only read, outputs are fully overwritten.
  *   Stream     a hipStream_t passed as void*; NULL is the default stream.  Work is only
  *              enqueued: nothing synchronises, allocates or frees device memory, and the
- *              library keeps no mutable global state.
+ *              library keeps no mutable global state (apart from fa_bwd_noalloc's static
+ *              scratch array, see there).
  *   Errors     every argument is checked before anything is enqueued; on a non-zero
  *              status nothing was launched and no output was touched.  FA_ERR_HIP means a
  *              launch was rejected by the runtime.  Faults inside a kernel surface at the
@@ -80,7 +81,8 @@ enum fa_status {
   FA_ERR_HIP = 9,          /* the HIP runtime rejected a launch */
   FA_ERR_TOO_LARGE = 10,   /* a size exceeds the 32-bit index range the kernels use */
   FA_ERR_ALIAS = 11,       /* an output buffer overlaps another buffer of the call */
-  FA_ERR_SPLIT = 12        /* a split / part count is out of range */
+  FA_ERR_SPLIT = 12,       /* a split / part count is out of range */
+  FA_ERR_SCRATCH = 13      /* fa_bwd_noalloc: the call needs more than FA_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -180,6 +182,24 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
 int fa_bwd_postprocess(void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
                        void* stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace: for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, outputs, errors and kernels as fa_bwd, whose workspace here is
+ * a device array inside the library: FA_NOALLOC_SCRATCH_BYTES (80 MiB) on each GPU the library
+ * runs on, held until the process ends.  Its address is resolved on the first call on a device
+ * (the stream's device, or the current one for a NULL stream); a failure to resolve it is
+ * FA_ERR_HIP.  A call whose fa_bwd_workspace_size(...) exceeds the array returns FA_ERR_SCRATCH
+ * and enqueues nothing.  Every call on one GPU shares that GPU's array, and the kernels write
+ * every part of it they read before reading it (no part needs to start at zero): calls that may
+ * overlap on one GPU (different streams, or graphs replayed concurrently) race and must be
+ * ordered by the caller.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (80u * 1024u * 1024u)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t N, int64_t D, float softmax_scale, int causal, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ STATUS = {
     "FA_OK": 0, "FA_ERR_NULL_POINTER": 1, "FA_ERR_BAD_SHAPE": 2, "FA_ERR_HEAD_DIM": 3,
     "FA_ERR_GQA": 4, "FA_ERR_DTYPE": 5, "FA_ERR_SCALE": 6, "FA_ERR_ALIGNMENT": 7,
     "FA_ERR_WORKSPACE": 8, "FA_ERR_HIP": 9, "FA_ERR_TOO_LARGE": 10, "FA_ERR_ALIAS": 11,
-    "FA_ERR_SPLIT": 12,
+    "FA_ERR_SPLIT": 12, "FA_ERR_SCRATCH": 13,
 }
 
 # Fake, aligned, non-null "device" addresses: every call below fails validation before any
@@ -62,7 +62,7 @@ def test_header_status_values_match():
 
 def test_version_and_strings(lib):
     assert fa.fa_version() == 10100
-    for code in range(13):
+    for code in range(14):
         s = fa.fa_status_string(code)
         assert s and s != "unknown status"
     assert fa.fa_status_string(999) == "unknown status"
@@ -241,3 +241,23 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
     with pytest.raises(RuntimeError):
         fa.fa_fwd(q, q, q)
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    """fa_bwd_noalloc: invalid shapes report fa_bwd's status, and a call that needs more than
+    the static scratch returns FA_ERR_SCRATCH, both before any HIP call (no GPU here)."""
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"]
+    p = [ptr(i) for i in range(len(names))]
+    call = lambda B, Hq, Hkv, N, D: lib.fa_bwd_noalloc(*p, B, Hq, Hkv, N, D, 0.1, 1, 1, None)
+    assert call(1, 2, 2, 256, 80) == STATUS["FA_ERR_HEAD_DIM"]
+    assert call(0, 2, 2, 256, 64) == STATUS["FA_ERR_BAD_SHAPE"]
+    assert call(1, 6, 4, 256, 64) == STATUS["FA_ERR_GQA"]
+    # grouped heads at N = 8192, D = 128: 128 MiB of fp32 dK/dV partials
+    assert fa.fa_bwd_workspace_size(1, 16, 4, 8192, 128) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert call(1, 16, 4, 8192, 128) == STATUS["FA_ERR_SCRATCH"]
+    # every configured workload fits
+    from exact_attention_fa_amd.inputs import WORKLOADS
+    for shapes in WORKLOADS.values():
+        for sh in shapes:
+            assert fa.fa_bwd_workspace_size(sh.B, sh.Hq, sh.Hkv, sh.N, sh.D) <= fa.FA_NOALLOC_SCRATCH_BYTES, sh
+
