@@ -211,17 +211,28 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   // S^T_j = K_j Q^T (register i of block (kb, qb) holds key j*BC + kb*32 + (i/8)*16 + g*8 + i%8
   // against query qi[qb]), with valu(i * QB + qb) run under the MFMA of fragment i, block qb.
-  auto scores = [&](const char* __restrict__ tK, f32x16 (&s)[2][QB], auto&& valu) FA_INL {
+  // With PRE its first RD fragments arrive in `pre` (read during the phase before); with POST
+  // its last RD steps, which have no fragment of their own left to read, read the next phase's
+  // first fragments next(r) into `post`.  pv() below takes the same two options.
+  auto scores = [&](auto pre_tag, auto post_tag, const char* __restrict__ tK, f32x16 (&s)[2][QB], auto&& valu,
+                    const u32x4 (&pre)[RD], auto&& next, u32x4 (&post)[RD]) FA_INL {
+    constexpr bool PRE = decltype(pre_tag)::value, POST = decltype(post_tag)::value;
     constexpr int NS = 2 * KST;
     u32x4 ring[RD + 1];
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
-      ring[i] = kfrag(tK, i);  // in use order, so each wait is partial
+      if constexpr (PRE)
+        ring[i] = pre[i];
+      else
+        ring[i] = kfrag(tK, i);  // in use order, so each wait is partial
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (i + RD < NS) ring[(i + RD) % (RD + 1)] = kfrag(tK, i + RD);
+      if (i + RD < NS)
+        ring[(i + RD) % (RD + 1)] = kfrag(tK, i + RD);
+      else if constexpr (POST)
+        post[i + RD - NS] = next(i + RD - NS);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -241,7 +252,9 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   // O^T += V^T P^T (A = V^T: rows d, k = keys, read transposed from the V tile), with
   // valu(i * QB + qb) run under the MFMA of fragment i, block qb.
-  auto pv = [&](const char* __restrict__ tV, u32x4 (&pb)[2][2][QB], auto&& valu) FA_INL {
+  auto pv = [&](auto pre_tag, auto post_tag, const char* __restrict__ tV, u32x4 (&pb)[2][2][QB], auto&& valu,
+                const u32x4 (&pre)[RD], auto&& next, u32x4 (&post)[RD]) FA_INL {
+    constexpr bool PRE = decltype(pre_tag)::value, POST = decltype(post_tag)::value;
     constexpr int NS = DB * 4;
     if constexpr (AGPR) {
       reg_fence(acc, true, false);
@@ -250,12 +263,18 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     u32x4 ring[RD + 1];
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
-      ring[i] = vfrag(tV, i);  // in use order, so each wait is partial
+      if constexpr (PRE)
+        ring[i] = pre[i];
+      else
+        ring[i] = vfrag(tV, i);  // in use order, so each wait is partial
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (i + RD < NS) ring[(i + RD) % (RD + 1)] = vfrag(tV, i + RD);
+      if (i + RD < NS)
+        ring[(i + RD) % (RD + 1)] = vfrag(tV, i + RD);
+      else if constexpr (POST)
+        post[i + RD - NS] = next(i + RD - NS);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -358,11 +377,16 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // and adds its two values.  fp16 sums the rounded pair in one dot2 (relative rounding 2^-12,
   // far inside the LSE tolerance even for a row with one visible key); bf16 rounding (2^-9) is
   // not, so bf16 sums the fp32 values.
+  // (The rare path rewrites every packed operand, so the compiler would sink the packing into
+  // the common path after the check, where it runs between the two MFMA phases with the
+  // matrix pipe idle; an empty asm statement that consumes each packed pair keeps it here.)
   float rs[QB];
   auto pack_unit = [&](u32x4 (&pb)[2][2][QB], int u) FA_INL {
     const int qb = u % QB, v = u / QB;
     const int kb = v >> 3, t2 = (v >> 2) & 1, pr = v & 3, e = t2 * 8 + pr * 2;
-    pb[kb][t2][qb][pr] = TR::pack(p[kb][qb][e], p[kb][qb][e + 1]);
+    uint32_t w = TR::pack(p[kb][qb][e], p[kb][qb][e + 1]);
+    asm volatile("" : "+v"(w));
+    pb[kb][t2][qb][pr] = w;
     if constexpr (std::is_same<TR, F16>::value)
       rs[qb] = TR::add_pair(pb[kb][t2][qb][pr], rs[qb]);
     else
@@ -458,16 +482,21 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int qb = 0; qb < QB; ++qb) p[kb][qb] = s[kb][qb];
   };
 
+  // First K fragments of the next step's S phase, read during this step's last P V MFMAs
+  // (two-step lead only: K_{j+1} is complete at step j's barrier).
+  u32x4 kpre[RD];
+  u32x4 unused[RD];
+  auto no_next = [](int) FA_INL { return u32x4{0u, 0u, 0u, 0u}; };
+  using Yes = std::true_type;
+  using No = std::false_type;
   auto step = [&](auto kind_tag, const int j, char* __restrict__ nK, char* __restrict__ nV,
                   const char* __restrict__ tK, const char* __restrict__ tV,
-                  const char* __restrict__ pK) FA_INL {
+                  const char* __restrict__ pK, const char* __restrict__ fK) FA_INL {
     constexpr Kind KIND = decltype(kind_tag)::value;
-    // this wave's loads of K_j and V_{j-1} have landed (the loads of the following DIST - 1
-    // steps may stay in flight: loads retire in issue order) ...
+    // this wave's loads of K_j and V_{j-1} have landed, and with two steps of lead also K_{j+1}
+    // (the load of V_j may stay in flight: loads retire in issue order) ...
     if constexpr (DIST == 2) {
-      if (j + 1 < Tg)
-        wait_vmcnt<2 * TI>();
-      else if (j < Tg)
+      if (j < Tg)
         wait_vmcnt<TI>();
       else
         wait_vmcnt<0>();
@@ -495,21 +524,31 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       // of a masked tile come after its S MFMAs.
       // The units are spread evenly over the MFMAs of each phase.
       constexpr int NSM = 2 * KST * QB, NPV = DB * 4 * QB, FIRST = kSmExp0, NP = 16 * QB;
-      scores(tK, s, [&](int i) FA_INL {
+      u32x4 vpre[RD];
+      auto packs = [&](int i) FA_INL {
 #pragma unroll
         for (int u = 0; u < NP; ++u)
           if (u * NSM / NP == i) pack_unit(pb, u);
-      });
+      };
+      auto vnext = [&](int r) FA_INL { return vfrag(tV, r); };
+      if constexpr (DIST == 2)
+        scores(Yes{}, Yes{}, tK, s, packs, kpre, vnext, vpre);
+      else
+        scores(No{}, Yes{}, tK, s, packs, unused, vnext, vpre);
       check(std::false_type{}, pK, j - 1, pb);
       add_rs();
       if constexpr (KIND == kSteadyMasked) mask(j, s);
       // (the steady steps run exp2 units only, all of equal weight)
       constexpr int NX = (kSmUnits - FIRST) * QB;
-      pv(tV, pb, [&](int i) FA_INL {
+      auto exps = [&](int i) FA_INL {
 #pragma unroll
         for (int x = 0; x < NX; ++x)
           if (x * NPV / NX == i) softmax_unit(s, FIRST * QB + x);
-      });
+      };
+      if constexpr (DIST == 2 && KIND == kSteady)
+        pv(Yes{}, Yes{}, tV, pb, exps, vpre, [&](int r) FA_INL { return kfrag(fK, r); }, kpre);
+      else
+        pv(Yes{}, No{}, tV, pb, exps, vpre, no_next, unused);
       keep_p(s);
     } else if constexpr (KIND == kFirst || KIND == kFirstMasked) {
       f32x16 s[2][QB];
@@ -517,11 +556,15 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-      scores(tK, s, [](int) FA_INL {});
+      scores(No{}, No{}, tK, s, [](int) FA_INL {}, unused, no_next, unused);
       if constexpr (KIND == kFirstMasked) mask(j, s);
       softmax_all(s);
       need = false;  // O is still zero
       keep_p(s);
+      if constexpr (DIST == 2 && KIND == kFirst) {  // the next step computes S: K_1 is complete
+#pragma unroll
+        for (int r = 0; r < RD; ++r) kpre[r] = kfrag(fK, r);
+      }
     } else if constexpr (KIND == kDrain) {
       u32x4 pb[2][2][QB];
       zero_rs();
@@ -529,7 +572,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int u = 0; u < 16 * QB; ++u) pack_unit(pb, u);
       check(std::true_type{}, pK, j - 1, pb);
       add_rs();
-      pv(tV, pb, [](int) FA_INL {});
+      pv(No{}, No{}, tV, pb, [](int) FA_INL {}, unused, no_next, unused);
     }
   };
 
@@ -544,7 +587,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   char* vf = sV;
   char* vd = sV + (DIST - 1) * TILE;
   auto run = [&](auto kind_tag, int j) FA_INL {
-    step(kind_tag, j, kd, vd, kc, vp, kp);
+    step(kind_tag, j, kd, vd, kc, vp, kp, kf);
     char* t;
     if constexpr (DIST == 2) {
       t = kp, kp = kc, kc = kf, kf = kd, kd = t;
