@@ -213,10 +213,12 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // against query qi[qb]), with valu(i * QB + qb) run under the MFMA of fragment i, block qb.
   // With PRE its first RD fragments arrive in `pre` (read during the phase before); with POST
   // its last RD steps, which have no fragment of their own left to read, read the next phase's
-  // first fragments next(r) into `post`.  pv() below takes the same two options.
+  // first fragments next(r) into `post`.  LASTNOP: the wait states the last MFMA carries (the
+  // steady steps first read its result half a phase later).  pv() below takes the same options.
   auto scores = [&](auto pre_tag, auto post_tag, const char* __restrict__ tK, f32x16 (&s)[2][QB], auto&& valu,
-                    const u32x4 (&pre)[RD], auto&& next, u32x4 (&post)[RD]) FA_INL {
+                    const u32x4 (&pre)[RD], auto&& next, u32x4 (&post)[RD], auto nop_tag) FA_INL {
     constexpr bool PRE = decltype(pre_tag)::value, POST = decltype(post_tag)::value;
+    constexpr int LASTNOP = decltype(nop_tag)::value;
     constexpr int NS = 2 * KST;
     u32x4 ring[RD + 1];
 #pragma unroll
@@ -241,7 +243,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         else if (i % KST == 0)  // (the loops are unrolled: one call remains per MFMA)
           mfma_va0<TR, kNopNone>(s[i / KST][qb], ring[i % (RD + 1)], qf[qb][i % KST]);
         else if (i == NS - 1 && qb == QB - 1)
-          mfma_va<TR, kNopAfter>(s[i / KST][qb], ring[i % (RD + 1)], qf[qb][i % KST]);
+          mfma_va<TR, LASTNOP>(s[i / KST][qb], ring[i % (RD + 1)], qf[qb][i % KST]);
         else
           mfma_va<TR, kNopNone>(s[i / KST][qb], ring[i % (RD + 1)], qf[qb][i % KST]);
         valu(i * QB + qb);
@@ -253,8 +255,9 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // O^T += V^T P^T (A = V^T: rows d, k = keys, read transposed from the V tile), with
   // valu(i * QB + qb) run under the MFMA of fragment i, block qb.
   auto pv = [&](auto pre_tag, auto post_tag, const char* __restrict__ tV, u32x4 (&pb)[2][2][QB], auto&& valu,
-                const u32x4 (&pre)[RD], auto&& next, u32x4 (&post)[RD]) FA_INL {
+                const u32x4 (&pre)[RD], auto&& next, u32x4 (&post)[RD], auto nop_tag) FA_INL {
     constexpr bool PRE = decltype(pre_tag)::value, POST = decltype(post_tag)::value;
+    constexpr int LASTNOP = decltype(nop_tag)::value;
     constexpr int NS = DB * 4;
     if constexpr (AGPR) {
       reg_fence(acc, true, false);
@@ -284,7 +287,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           if (i == 0 && qb == 0)
             mfma_av<TR, kNopBefore>(o, a, b);
           else if (i == NS - 1 && qb == QB - 1)
-            mfma_av<TR, kNopAfter>(o, a, b);
+            mfma_av<TR, LASTNOP>(o, a, b);
           else
             mfma_av<TR, kNopNone>(o, a, b);
         }
@@ -399,6 +402,9 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // O *= alpha (rare).  Accumulators in AGPRs pass through VGPRs one block at a time, with
   // each move written out so that the accumulators are never allocated to VGPRs.
   auto scale_acc = [&]() FA_INL {
+    // (the steady steps' last P V MFMA carries no wait states, so this rare reader waits;
+    // the library's tests walk every path of the compiled code from each written-out MFMA)
+    if constexpr (AGPR) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -508,8 +514,12 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       scale_acc();
       need = false;
     }
-    if (j + DIST < Tg) issue(rK, j + DIST, nK);
-    if (j + DIST - 1 < Tg) issue(rV, j + DIST - 1, nV);
+    // The steady steps issue the next tiles' loads under their first S MFMAs.
+    constexpr bool LATE_ISSUE = KIND == kSteady || KIND == kSteadyMasked;
+    if constexpr (!LATE_ISSUE) {
+      if (j + DIST < Tg) issue(rK, j + DIST, nK);
+      if (j + DIST - 1 < Tg) issue(rV, j + DIST - 1, nV);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (KIND == kSteady || KIND == kSteadyMasked) {
       // [S_j MFMAs | pack P_{j-1}]  [P_{j-1} V_{j-1} MFMAs | softmax of S_j]
@@ -526,15 +536,19 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       constexpr int NSM = 2 * KST * QB, NPV = DB * 4 * QB, FIRST = kSmExp0, NP = 16 * QB;
       u32x4 vpre[RD];
       auto packs = [&](int i) FA_INL {
+        if (i == 1 && j + DIST < Tg) issue(rK, j + DIST, nK);
+        if (i == 3 && j + DIST - 1 < Tg) issue(rV, j + DIST - 1, nV);
 #pragma unroll
         for (int u = 0; u < NP; ++u)
           if (u * NSM / NP == i) pack_unit(pb, u);
       };
       auto vnext = [&](int r) FA_INL { return vfrag(tV, r); };
+      // (the last S MFMA's result is first read half a phase later, unless the masks follow)
+      constexpr int SNOP = KIND == kSteady ? kNopNone : kNopAfter;
       if constexpr (DIST == 2)
-        scores(Yes{}, Yes{}, tK, s, packs, kpre, vnext, vpre);
+        scores(Yes{}, Yes{}, tK, s, packs, kpre, vnext, vpre, std::integral_constant<int, SNOP>{});
       else
-        scores(No{}, Yes{}, tK, s, packs, unused, vnext, vpre);
+        scores(No{}, Yes{}, tK, s, packs, unused, vnext, vpre, std::integral_constant<int, SNOP>{});
       check(std::false_type{}, pK, j - 1, pb);
       add_rs();
       if constexpr (KIND == kSteadyMasked) mask(j, s);
@@ -545,10 +559,12 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int x = 0; x < NX; ++x)
           if (x * NPV / NX == i) softmax_unit(s, FIRST * QB + x);
       };
+      // (the accumulators' next readers outside MFMAs, scale_acc and the drain, wait themselves)
+      using NoWait = std::integral_constant<int, kNopNone>;
       if constexpr (DIST == 2 && KIND == kSteady)
-        pv(Yes{}, Yes{}, tV, pb, exps, vpre, [&](int r) FA_INL { return kfrag(fK, r); }, kpre);
+        pv(Yes{}, Yes{}, tV, pb, exps, vpre, [&](int r) FA_INL { return kfrag(fK, r); }, kpre, NoWait{});
       else
-        pv(Yes{}, No{}, tV, pb, exps, vpre, no_next, unused);
+        pv(Yes{}, No{}, tV, pb, exps, vpre, no_next, unused, NoWait{});
       keep_p(s);
     } else if constexpr (KIND == kFirst || KIND == kFirstMasked) {
       f32x16 s[2][QB];
@@ -556,7 +572,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-      scores(No{}, No{}, tK, s, [](int) FA_INL {}, unused, no_next, unused);
+      scores(No{}, No{}, tK, s, [](int) FA_INL {}, unused, no_next, unused,
+             std::integral_constant<int, kNopAfter>{});
       if constexpr (KIND == kFirstMasked) mask(j, s);
       softmax_all(s);
       need = false;  // O is still zero
@@ -572,7 +589,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int u = 0; u < 16 * QB; ++u) pack_unit(pb, u);
       check(std::true_type{}, pK, j - 1, pb);
       add_rs();
-      pv(No{}, No{}, tV, pb, [](int) FA_INL {}, unused, no_next, unused);
+      pv(No{}, No{}, tV, pb, [](int) FA_INL {}, unused, no_next, unused,
+         std::integral_constant<int, kNopAfter>{});
     }
   };
 
