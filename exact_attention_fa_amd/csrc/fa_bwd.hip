@@ -585,7 +585,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // ---- pipeline pieces
   // S^T and dP^T of one tile (register i <-> key (i/8)*16 + g*8 + i%8), with valu(i) run
   // under MFMA i.
-  auto sdp = [&](const char* tK, const char* tV, f32x16& s, f32x16& dp, auto&& valu) FA_INL {
+  // dQ^T fragment i of tile tK (i = db*2 + t2): K^T read transposed.
+  auto qfrag = [&](const char* tK, int i) FA_INL {
+    return lds_tr8(tK + sl_off<BC>((i & 1) * 16, (i >> 1) * 32), trl);
+  };
+  // With POST the last RD steps read the dQ phase's first fragments (of tile pK) into post.
+  auto sdp = [&](auto post_tag, const char* tK, const char* tV, f32x16& s, f32x16& dp, auto&& valu,
+                 const char* pK, u32x4 (&post)[RD]) FA_INL {
+    constexpr bool POST = decltype(post_tag)::value;
     auto frag = [&](int i) FA_INL {  // i = kk*2 + (0: K, 1: V)
       const int kk = i >> 1;
       return lds_ld128(((i & 1) ? tV : tK) + sl_off<BC>(0, (kk >> 1) * 32) + koff[kk & 1]);
@@ -598,7 +605,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 #pragma unroll
     for (int i = 0; i < 2 * KST; ++i) {
-      if (i + RD < 2 * KST) ring[(i + RD) % (RD + 1)] = frag(i + RD);
+      if (i + RD < 2 * KST)
+        ring[(i + RD) % (RD + 1)] = frag(i + RD);
+      else if constexpr (POST)
+        post[i + RD - 2 * KST] = qfrag(pK, i + RD - 2 * KST);
       __builtin_amdgcn_sched_barrier(0);
       if (i & 1)
         dp = TR::mfma(ring[i % (RD + 1)], of[i >> 1], dp);
@@ -625,15 +635,17 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       dt = ds;
   };
   // dQ^T += K^T dS^T of one tile (2*DB MFMAs), A operand read transposed from the K tile.
-  auto dqm = [&](const char* tK, const u32x4 (&dsb)[2]) FA_INL {
-    auto frag = [&](int i) FA_INL {  // i = db*2 + t2
-      return lds_tr8(tK + sl_off<BC>((i & 1) * 16, (i >> 1) * 32), trl);
-    };
+  auto dqm = [&](auto pre_tag, const char* tK, const u32x4 (&dsb)[2], const u32x4 (&pre)[RD]) FA_INL {
+    constexpr bool PRE = decltype(pre_tag)::value;
+    auto frag = [&](int i) FA_INL { return qfrag(tK, i); };  // i = db*2 + t2
     constexpr int NS = 2 * DB;
     u32x4 ring[RD + 1];
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
-      ring[i] = frag(i);  // in use order, so each wait is partial
+      if constexpr (PRE)
+        ring[i] = pre[i];
+      else
+        ring[i] = frag(i);  // in use order, so each wait is partial
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -660,23 +672,27 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     else
       wait_vmcnt<0>();
     dma_barrier();
-    if (j + 3 < Tg) issue(j + 3, dK_, dV_);
+    if constexpr (KIND != kSteady)
+      if (j + 3 < Tg) issue(j + 3, dK_, dV_);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 dsb[2];
     float dt;
+    u32x4 qpre[RD];
     if constexpr (KIND == kSteady) {
       ns = f32x16{};
       ndp = f32x16{};
-      sdp(nK, nV, ns, ndp, [&](int i) FA_INL {
+      // the next tile's loads go out under the first MFMAs
+      sdp(std::true_type{}, nK, nV, ns, ndp, [&](int i) FA_INL {
+        if (i == 1 && j + 3 < Tg) issue(j + 3, dK_, dV_);
 #pragma unroll
         for (int w = 0; w < 16; ++w)
           if (w * 2 * KST / 16 == i) ds_unit(std::false_type{}, j, cs, cdp, dsb, dt, w);
-      });
-      dqm(tK, dsb);
+      }, tK, qpre);
+      dqm(std::true_type{}, tK, dsb, qpre);
     } else if constexpr (KIND == kLast || KIND == kLastMasked) {
 #pragma unroll
       for (int w = 0; w < 16; ++w) ds_unit(std::bool_constant<KIND == kLastMasked>{}, j, cs, cdp, dsb, dt, w);
-      dqm(tK, dsb);
+      dqm(std::false_type{}, tK, dsb, qpre);
     }
   };
 
@@ -717,7 +733,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (Twg > 0) {
     sa = f32x16{};
     dpa = f32x16{};
-    sdp(kb0, vb0, sa, dpa, [](int) FA_INL {});
+    u32x4 unused[RD];
+    sdp(std::false_type{}, kb0, vb0, sa, dpa, [](int) FA_INL {}, kb0, unused);
   }
   // Every wave takes exactly `half` steps (one barrier each); the group's last computed tile
   // is the only one that can need masks.
