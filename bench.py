@@ -307,7 +307,48 @@ def _short(name):
     return name
 
 
-def summarize(kind, dirs, skip=0):
+_STAGE_OF = {"fwd_kernel": "fwd", "bwd_pre_kernel": "bwd_preprocess", "bwd_dkdv_kernel": "bwd_dkdv",
+             "bwd_dq_kernel": "bwd_dq"}
+
+
+def _counter_avg(directory, counter):
+    from collections import defaultdict
+    vals = defaultdict(list)
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: statistics.fmean(v) for k, v in vals.items()}
+
+
+def _traffic(dirs, copy_bytes, workload):
+    """The blocks that profiles/traffic_<stage>_<workload>.txt hold (see summarize)."""
+    from exact_attention_fa_amd.inputs import WORKLOADS
+    name, variant = WORKLOAD_KEYS[workload]
+    alg = algorithmic_bytes(WORKLOADS[name][variant])
+    fetch, write = _counter_avg(dirs[0], "FETCH_SIZE"), _counter_avg(dirs[1], "WRITE_SIZE")
+    cfetch, cwrite = _counter_avg(dirs[2], "FETCH_SIZE"), _counter_avg(dirs[3], "WRITE_SIZE")
+    copy = [k for k in cfetch if "copy" in k.lower()]
+    if len(copy) != 1 or copy[0] not in cwrite:
+        raise SystemExit(f"expected one copy kernel in the calibration runs, found {sorted(cfetch)}")
+    fscale = copy_bytes / (cfetch[copy[0]] * 1024.0)
+    wscale = copy_bytes / (cwrite[copy[0]] * 1024.0)
+    for k in sorted(fetch):
+        stage = _STAGE_OF.get(k.split("<", 1)[0])
+        if stage is None or k not in write:
+            continue
+        rd, wr = fetch[k] * 1024.0 * fscale, write[k] * 1024.0 * wscale
+        print(f"# {stage}: {k}")
+        for key, val in (("kernel", stage), ("workload", workload),
+                         ("fetch_size_kib", f"{fetch[k]:.1f}"), ("write_size_kib", f"{write[k]:.1f}"),
+                         ("fetch_scale", f"{fscale:.5f}"), ("write_scale", f"{wscale:.5f}"),
+                         ("hbm_read_bytes", f"{rd:.0f}"), ("hbm_write_bytes", f"{wr:.0f}"),
+                         ("hbm_bytes_per_launch", f"{rd + wr:.0f}"),
+                         ("algorithmic_bytes_per_launch", alg[stage]),
+                         ("source_sha256_16", source_hash(stage))):
+            print(f"{key} = {val}")
+
+
+def summarize(kind, dirs, skip=0, copy_bytes=0, workload=None):
     """Summary lines from rocprofv3 CSV output, per kernel (the template name shortened):
       trace DIR       average dispatch duration (us) over the dispatches after the first `skip`
       counters DIR..  per-dispatch averages of every collected counter (one or more runs)
@@ -315,8 +356,18 @@ def summarize(kind, dirs, skip=0):
                       timestamps: MFMA busy fraction per SIMD (busy cycles / 1024 SIMDs / the
                       kernel's cycles) and the sustained shader clock (GRBM_GUI_ACTIVE / 8 XCDs /
                       duration)
-    Prints `kernel: key = value` lines; no GPU is needed."""
+      traffic F W CF CW   HBM bytes per launch from a FETCH_SIZE run (F) and a WRITE_SIZE run (W)
+                      of the workload, each scaled by what the same counter reads for a plain copy
+                      of `copy_bytes` bytes (runs CF and CW), next to the stage's algorithmic bytes
+    Prints `kernel: key = value` lines (traffic: a block of `key = value` lines per kernel); no
+    GPU is needed."""
     from collections import defaultdict
+    if kind == "traffic":
+        if len(dirs) != 4 or not copy_bytes or workload is None:
+            raise SystemExit("--summarize traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR "
+                             "needs --workload and --copy-calibration BYTES")
+        _traffic(dirs, copy_bytes, workload)
+        return
     if kind == "trace":
         rows = _csv_rows(dirs[0], "kernel_trace.csv")
         dur = defaultdict(list)
@@ -364,12 +415,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--ceilings", action="store_true", help="measure library GEMM and HBM rates and exit")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
-                    help="summarise rocprofv3 CSV output: trace DIR | counters DIR... | busy DIR...")
+                    help="summarise rocprofv3 CSV output: trace DIR | counters DIR... | busy DIR... | "
+                         "traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR")
     ap.add_argument("--skip", type=int, default=0, help="with --summarize trace: dispatches to skip")
     args = ap.parse_args()
 
     if args.summarize:
-        summarize(args.summarize[0], args.summarize[1:], args.skip)
+        summarize(args.summarize[0], args.summarize[1:], args.skip, args.copy_calibration,
+                  args.workload if args.summarize[0] == "traffic" else None)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

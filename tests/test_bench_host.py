@@ -89,3 +89,23 @@ def test_busy_summary_needs_matching_source(tmp_path, monkeypatch):
     with open(tmp_path / rel, "w") as f:
         f.write("int y;\n")
     assert bench.counter_summary("fwd", "w") is None
+
+
+def test_traffic_summary_scales_by_copy(tmp_path, capsys):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled so that the copy reads and writes its size."""
+    name = "void fa::(anonymous namespace)::bwd_dkdv_kernel<fa::Bf16, 128, false, false>(unsigned short const*, int)"
+    copy = "__amd_rocclr_copyBuffer"
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    _write(str(tmp_path / "f" / "h" / "run_counter_collection.csv"), hdr, [[name, "FETCH_SIZE", 1000.0]])
+    _write(str(tmp_path / "w" / "h" / "run_counter_collection.csv"), hdr, [[name, "WRITE_SIZE", 300.0]])
+    _write(str(tmp_path / "cf" / "h" / "run_counter_collection.csv"), hdr, [[copy, "FETCH_SIZE", 512.0]])
+    _write(str(tmp_path / "cw" / "h" / "run_counter_collection.csv"), hdr, [[copy, "WRITE_SIZE", 1024.0]])
+    dirs = [str(tmp_path / d) for d in ("f", "w", "cf", "cw")]
+    bench.summarize("traffic", dirs, copy_bytes=1024 * 1024, workload="fwd_bf16_n16384")
+    out = capsys.readouterr().out
+    assert "kernel = bwd_dkdv" in out and "fetch_scale = 2.00000" in out and "write_scale = 1.00000" in out
+    assert f"hbm_bytes_per_launch = {2000 * 1024 + 300 * 1024}" in out
+    from exact_attention_fa_amd.inputs import WORKLOADS
+    alg = bench.algorithmic_bytes(WORKLOADS["fwd_bf16_long"][1])["bwd_dkdv"]
+    assert f"algorithmic_bytes_per_launch = {alg}" in out
+    assert f"source_sha256_16 = {bench.source_hash('bwd_dkdv')}" in out
