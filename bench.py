@@ -40,7 +40,8 @@ including the recompute of S), halved when causal.
 `--copy-calibration BYTES` instead runs a plain device-to-device copy of BYTES bytes five
 times (the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
 `--ceilings` instead measures what the GPU sustains on plain library work (8192^3 bf16 and
-fp16 GEMMs, 2 GiB HBM read and copy), context for the roofline fractions, and exits.
+fp16 GEMMs, 2 GiB HBM read and copy), and the backward preprocess at the default size and at
+8x its rows, context for the roofline fractions, and exits.
 `--summarize KIND DIR...` reads rocprofv3 CSV output (no GPU) and prints the summary lines that
 the files under profiles/ hold (see summarize()).
 """
@@ -157,6 +158,23 @@ def machine_ceilings():
     y = torch.empty_like(x)
     t = timed(lambda: y.copy_(x), 20)
     out["hbm_copy_read_plus_write_gbs"] = round(2 * x.numel() * 2 / t / 1e9, 1)
+    del x, y
+    # The backward preprocess (a pure stream: O and dO read, two fp32 values per row written) at
+    # the default workload's size and at 8x its rows: how much of its rate the size sets.
+    import exact_attention_fa_amd as fa
+    from exact_attention_fa_amd.inputs import Shape
+    fa.load_library()
+    for B in (1, 8):
+        H, N, D = 16, 16384, 128
+        o = torch.randn((B, H, N, D), device="cuda").to(torch.bfloat16)
+        do = torch.randn((B, H, N, D), device="cuda").to(torch.bfloat16)
+        lse = torch.zeros((B, H, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, H, N, D), dtype=torch.uint8, device="cuda")
+        t = timed(lambda: fa.fa_bwd_preprocess(o, do, lse, ws, H), 20)
+        nbytes = algorithmic_bytes(Shape(B, H, H, N, D, "bf16", False))["bwd_preprocess"]
+        out[f"bwd_preprocess_B{B}_H16_N16384_MiB"] = round(nbytes / 2 ** 20, 1)
+        out[f"bwd_preprocess_B{B}_H16_N16384_gbs"] = round(nbytes / t / 1e9, 1)
+        del o, do, lse, ws
     out["clock_after"] = gpu_clock()
     print(json.dumps(out), flush=True)
 
