@@ -49,7 +49,14 @@ constexpr int kDqBC = 32;     // dQ kernel: keys per K/V tile
 // bytes of O and of dO each; a thread keeps the loads of kPreRows rows in flight, and at most
 // kPreBlocks workgroups stride over the rows (streaming reads on this GPU reach their best
 // rate with a few thousand resident workgroups, not one short-lived workgroup per 64 rows).
+// The loads are non-temporal (each byte is read once): 11% faster than ordinary loads at
+// 131 MiB and at 1 GiB.  (Four rows in flight per thread were 4% faster still at 131 MiB but
+// halve the workgroups of small grids, which then ran slower.)
 constexpr int kPreRows = 2, kPreBlocks = 2048;
+__device__ __forceinline__ u32x4 ld16_stream_if(const void* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)) : z;
+}
 template <typename TR, int HD>
 __global__ void __launch_bounds__(kThreads)
 bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
@@ -65,8 +72,8 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
     for (int u = 0; u < kPreRows; ++u) {
       const long long row = row0 + (long long)u * RPP;  // each pass reads RPP consecutive rows
       const bool ok = row < rows;
-      o[u] = ld16_if(O + (ok ? row : 0) * HD + part * 8, ok);
-      d[u] = ld16_if(dO + (ok ? row : 0) * HD + part * 8, ok);
+      o[u] = ld16_stream_if(O + (ok ? row : 0) * HD + part * 8, ok);
+      d[u] = ld16_stream_if(dO + (ok ? row : 0) * HD + part * 8, ok);
     }
 #pragma unroll
     for (int u = 0; u < kPreRows; ++u) {
