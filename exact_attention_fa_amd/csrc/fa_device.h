@@ -216,7 +216,8 @@ __device__ __forceinline__ void store_staged(const char* region, void* dst, int 
   for (int k = 0; k < R / RPI; ++k) {
     const int r = k * RPI + lane / CH, ch = lane % CH;
     const u32x4 v = lds_ld128(region + stage_off<RB>(r, ch));
-    if (r < n_valid) *reinterpret_cast<u32x4*>(static_cast<char*>(dst) + (size_t)r * STRIDE + ch * 16) = v;
+    // (non-temporal: the output is not read again here; 0.3-1.2% faster forward at N >= 4096)
+    if (r < n_valid) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<char*>(dst) + (size_t)r * STRIDE + ch * 16));
   }
 }
 
