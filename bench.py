@@ -18,9 +18,13 @@ Prints ONE JSON line on stdout:
                   launch over its HIP-event time, against the HBM peak
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
   kernel_*_ms     per-kernel average, median, minimum and maximum over the timed steps
-  mfma_util       MFMA busy fraction and sustained shader clock of the dominant kernel, from
-                  the committed hardware-counter summary under profiles/ (null when the
-                  kernel source has changed since the counters were taken)
+  mfma_util       MFMA (and VALU) busy fraction and sustained shader clock of the dominant
+                  kernel, from the committed hardware-counter summary under profiles/ (null
+                  when the kernel source has changed since the counters were taken)
+  measured_gemm   an 8192^3 library GEMM in the workload's dtype, run after the timed steps:
+                  the measured MFMA ceiling, with fwd and fwd+bwd as % of it
+  gpu_power_w     board power (sysfs hwmon, read in-process) before the warmup and after the
+                  timed steps
   gpu_clock       the shader clock level the driver reports (sysfs, read in-process) before
                   the warmup and after the timed steps
 
@@ -199,6 +203,49 @@ def gpu_clock():
     return out or None
 
 
+def gpu_power():
+    """Board power in watts from the amdgpu driver's hwmon files (power1_average, else
+    power1_input, in microwatts), read in this process, per card by PCI address; None where
+    they cannot be read."""
+    out = {}
+    try:
+        for card in sorted(os.listdir("/sys/class/drm")):
+            dev = os.path.join("/sys/class/drm", card, "device")
+            hw = os.path.join(dev, "hwmon")
+            if not card.startswith("card") or "-" in card or not os.path.isdir(hw):
+                continue
+            for h in sorted(os.listdir(hw)):
+                for name in ("power1_average", "power1_input"):
+                    path = os.path.join(hw, h, name)
+                    if os.path.exists(path):
+                        with open(path) as f:
+                            out[os.path.basename(os.path.realpath(dev))] = round(int(f.read().strip()) / 1e6, 1)
+                        break
+    except (OSError, ValueError):  # context only, never a reason to fail the run
+        return None
+    return out or None
+
+
+def measured_gemm_tflops(dtype_name):
+    """What a plain library GEMM sustains on this GPU right now, in the workload's dtype: an
+    8192^3 torch.matmul (hipBLASLt), 10 products after 3 warmups, timed with HIP events.  The
+    measured MFMA ceiling beside the spec peak."""
+    import torch
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype_name]
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(dt)
+    b = torch.randn(n, n, device="cuda").to(dt)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record()
+    e1.synchronize()
+    return 2 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+
+
 def copy_calibration(nbytes):
     import torch
     n = nbytes // 4
@@ -290,9 +337,12 @@ def counter_summary(kernel, workload):
     if kv.get("source_sha256_16") != source_hash(kernel):
         return None
     try:
-        return {"kernel": kernel, "mfma_busy_frac": float(kv["mfma_busy_frac"]),
-                "sclk_mhz_sustained": float(kv["sclk_mhz_sustained"]),
-                "source": f"profiles/busy_{kernel}_{workload}.txt"}
+        out = {"kernel": kernel, "mfma_busy_frac": float(kv["mfma_busy_frac"]),
+               "sclk_mhz_sustained": float(kv["sclk_mhz_sustained"]),
+               "source": f"profiles/busy_{kernel}_{workload}.txt"}
+        if "valu_busy_frac" in kv:
+            out["valu_busy_frac"] = float(kv["valu_busy_frac"])
+        return out
     except (KeyError, ValueError):
         return None
 
@@ -373,7 +423,8 @@ def summarize(kind, dirs, skip=0, copy_bytes=0, workload=None):
       busy DIR..      from SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE and the dispatches' own
                       timestamps: MFMA busy fraction per SIMD (busy cycles / 1024 SIMDs / the
                       kernel's cycles) and the sustained shader clock (GRBM_GUI_ACTIVE / 8 XCDs /
-                      duration)
+                      duration); with SQ_ACTIVE_INST_VALU also the VALU busy fraction (its
+                      4-cycle units summed over waves, per SIMD and kernel cycle)
       traffic F W CF CW   HBM bytes per launch from a FETCH_SIZE run (F) and a WRITE_SIZE run (W)
                       of the workload, each scaled by what the same counter reads for a plain copy
                       of `copy_bytes` bytes (runs CF and CW), next to the stage's algorithmic bytes
@@ -416,7 +467,10 @@ def summarize(kind, dirs, skip=0, copy_bytes=0, workload=None):
             continue
         cycles = gui / 8.0                       # per XCD: the kernel's duration in shader cycles
         busy = mfma / 1024.0 / cycles            # 1024 SIMDs (256 CUs x 4)
-        line = f"{k}: mfma_busy_frac = {busy:.4f}; gui_cycles_per_xcd = {cycles:.4g}"
+        line = f"{k}: mfma_busy_frac = {busy:.4f}"
+        if "SQ_ACTIVE_INST_VALU" in avg:         # counted in units of 4 cycles, summed over waves
+            line += f"; valu_busy_frac = {avg['SQ_ACTIVE_INST_VALU'] * 4.0 / 1024.0 / cycles:.4f}"
+        line += f"; gui_cycles_per_xcd = {cycles:.4g}"
         if dur_us:
             line += f"; dur_us = {dur_us:.1f}; sclk_mhz_sustained = {cycles / dur_us:.0f}"
         print(line)
@@ -430,6 +484,7 @@ def main():
     ap.add_argument("--workload", default="fwd_bf16_n16384", choices=sorted(WORKLOAD_KEYS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-ceiling", action="store_true", help="skip the library GEMM measured after the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--ceilings", action="store_true", help="measure library GEMM and HBM rates and exit")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
@@ -499,7 +554,7 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
-    clock_before = gpu_clock()
+    clock_before, power_before = gpu_clock(), gpu_power()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -512,7 +567,7 @@ def main():
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clock_after = gpu_clock()
+    clock_after, power_after = gpu_clock(), gpu_power()
 
     per_kernel = {kname: [] for kname in kernels}
     step_ms = []
@@ -583,6 +638,7 @@ def main():
         "kernel_min_ms": {kname: round(min(vals), 4) for kname, vals in per_kernel.items()},
         "kernel_max_ms": {kname: round(max(vals), 4) for kname, vals in per_kernel.items()},
         "gpu_clock": {"before": clock_before, "after": clock_after},
+        "gpu_power_w": {"before": power_before, "after": power_after},
         "mfma_util": None if latency_bound else counter_summary(dominant, args.workload),
         "roofline": roofline,
         "hbm": hbm,
@@ -597,6 +653,11 @@ def main():
             "step_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
             "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
         }
+    if not latency_bound and not args.no_gemm_ceiling:
+        g = measured_gemm_tflops(shape.dtype)
+        out["measured_gemm"] = {"tflops": round(g, 1), "what": f"8192^3 {shape.dtype} torch.matmul (hipBLASLt), after the timed steps",
+                                "fwd_pct": round(100 * out["fwd_tflops"] / g, 1),
+                                "fwd_bwd_pct": round(100 * value / g, 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, seed, args.cpu_budget)
     print(json.dumps(out), flush=True)

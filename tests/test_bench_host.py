@@ -35,6 +35,8 @@ def test_clock_query_spawns_nothing(monkeypatch):
     monkeypatch.setattr(os, "posix_spawn", refuse, raising=False)
     clk = bench.gpu_clock()  # None here (no GPU), or the sysfs levels
     assert clk is None or isinstance(clk, dict)
+    pw = bench.gpu_power()
+    assert pw is None or isinstance(pw, dict)
 
 
 def _write(path, header, rows):
@@ -60,6 +62,11 @@ def test_summaries_from_rocprof_csv(tmp_path, capsys):
     bench.summarize("busy", [str(tmp_path / "c")])
     out = capsys.readouterr().out
     assert "mfma_busy_frac = 0.5500" in out and "gui_cycles_per_xcd = 2e+06" in out
+    _write(str(tmp_path / "v" / "host" / "1" / "run_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+           rows[:2] + [[name, "SQ_ACTIVE_INST_VALU", 1024 * 2.0e6 / 4 * 0.3]])
+    bench.summarize("busy", [str(tmp_path / "v")])
+    out = capsys.readouterr().out
+    assert "valu_busy_frac = 0.3000" in out
 
 
 def test_workloads_and_bytes():
