@@ -265,3 +265,43 @@ def test_shard_causal_bf16_full():
     for name, g, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
         errs[name] = assert_grad_close(f64(g), r, name, str(shape))
     log("  errors", errs)
+
+
+def _random_cases(n, seed):
+    """Seeded shapes across the supported space: batch, MQA/GQA/MHA head ratios, ragged N
+    (log-uniform up to ~1500, including 1), both head dims and dtypes, causal or not, and the
+    default, zero, small, large or negative softmax scales.  Each case's oracle work is capped
+    (B * Hq * N^2 <= 4e7) so the whole sweep runs in well under a minute."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 1, 2, 3]))
+        grp = int(rng.choice([1, 1, 2, 3, 4, 8]))
+        N = int(np.clip(round(float(np.exp(rng.uniform(0.0, np.log(1500))))), 1, 1500))
+        D = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        causal = bool(rng.integers(0, 2))
+        kind = int(rng.integers(0, 5))
+        scale = None if kind < 2 else (0.0 if kind == 2 else float(np.round(rng.uniform(-0.25, 0.25), 4)))
+        if B * Hkv * grp * N * N > 4e7:
+            continue
+        cases.append((B, Hkv * grp, Hkv, N, D, dtype, causal, scale))
+    return cases
+
+
+RANDOM = _random_cases(64, 2026)
+
+
+@pytest.mark.parametrize("dims", RANDOM, ids=[f"B{b}H{hq}/{hk}N{n}D{d}{t}{'c' if cz else ''}s{sc}"
+                                              for b, hq, hk, n, d, t, cz, sc in RANDOM])
+def test_random_shapes_full(dims):
+    """A seeded sweep of shapes, each compared element by element with the oracle (forward and
+    backward)."""
+    from parity_util import full_check
+    B, Hq, Hkv, N, D, dtype, causal, scale = dims
+    shape = Shape(B, Hq, Hkv, N, D, dtype, causal)
+    log("random shape", shape, "scale", scale)
+    errs = full_check(shape, zlib.crc32(repr(dims).encode()) % (1 << 31), scale=scale)
+    log("  errors", errs)
