@@ -3,8 +3,8 @@
 
 A step is one pass of the whole path over one batch of synthetic input: the forward
 (fa_fwd_splitkv with the library's choice of key-range pieces, which is exactly fa_fwd
-except on grids too small to fill the GPU) and the backward (preprocess, dK/dV pass, dQ
-pass, postprocess) on the same stream.
+except on grids too small to fill the GPU) and the backward (fa_bwd: preprocess, dK/dV pass,
+dQ pass, postprocess) on the same stream.
 Inputs, outputs and workspace are allocated and resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout:
@@ -17,7 +17,8 @@ Prints ONE JSON line on stdout:
   hbm             the memory-bound stage (the backward preprocess): algorithmic bytes per
                   launch over its HIP-event time, against the HBM peak
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
-  kernel_*_ms     per-kernel average, median, minimum and maximum over the timed steps
+  kernel_*_ms     per-kernel average, median, minimum and maximum over K further steps timed
+                  kernel by kernel
   mfma_util       MFMA (and VALU) busy fraction and sustained shader clock of the dominant
                   kernel, from the committed hardware-counter summary under profiles/ (null
                   when the kernel source has changed since the counters were taken)
@@ -29,8 +30,10 @@ Prints ONE JSON line on stdout:
                   the warmup and after the timed steps
 
 `value` and `ms_per_step` use the median of the per-step HIP-event durations (the pages'
-protocol: warmups, then the median of the timed repetitions); `wall_ms_per_step` is the
-host wall time of the whole timed region divided by the steps.  The default workload is the
+protocol: warmups, then the median of the timed repetitions; one event pair per step);
+`wall_ms_per_step` is the host wall time of the whole timed region divided by the steps.
+The per-kernel figures (kernel_*_ms, fwd/bwd TFLOP/s, roofline, hbm) come from K further
+steps, after the timed region, with an event between every two kernels.  The default workload is the
 long non-causal bf16 sequence (B=1, H=16, N=16384, D=128).  The tiny fp16 workloads
 (`--workload tiny_fp16_nc` / `tiny_fp16_causal`, B=1, H=2, N=256, D=64) are latency-bound:
 their line adds microseconds per kernel and the step's algorithmic HBM bytes per second.
@@ -535,49 +538,56 @@ def main():
     kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_postprocess"]
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+        if ev is None:  # as a caller runs it: one forward call and one fa_bwd call
+            fa.fa_fwd_splitkv(q, k, v, causal=causal, softmax_scale=scale, n_split=n_split, workspace=fws, out=o,
+                              lse=lse)
+            fa.fa_bwd(q, k, v, o, do, lse, causal=causal, softmax_scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+            return
+        # kernel by kernel: fa_bwd's stages (the same launches) with an event between every two
+        ev[0].record(stream)
         fa.fa_fwd_splitkv(q, k, v, causal=causal, softmax_scale=scale, n_split=n_split, workspace=fws, out=o,
                           lse=lse)
-        if ev is not None:
-            ev[1].record(stream)
+        ev[1].record(stream)
         fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
-        if ev is not None:
-            ev[2].record(stream)
+        ev[2].record(stream)
         fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=causal, softmax_scale=scale)
-        if ev is not None:
-            ev[3].record(stream)
+        ev[3].record(stream)
         fa.fa_bwd_dq(q, k, v, do, dq, ws, causal=causal, softmax_scale=scale)
-        if ev is not None:
-            ev[4].record(stream)
+        ev[4].record(stream)
         fa.fa_bwd_postprocess(dk, dv, ws, Hq)
-        if ev is not None:
-            ev[5].record(stream)
+        ev[5].record(stream)
 
     clock_before, power_before = gpu_clock(), gpu_power()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps, bracketed by device synchronisation.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    # Timed region: exactly K steps, bracketed by device synchronisation, with one event pair
+    # per step (events between the kernels would add their own gaps to a latency-bound step).
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(evs[s])
+        sev[s][0].record(stream)
+        step()
+        sev[s][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     clock_after, power_after = gpu_clock(), gpu_power()
+    ms_per_step = statistics.median([a.elapsed_time(b) for a, b in sev])
 
+    # Per-kernel breakdown: K further steps through fa_bwd's stage entry points, with an event
+    # after every kernel.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
     per_kernel = {kname: [] for kname in kernels}
-    step_ms = []
     for ev in evs:
         for i, kname in enumerate(kernels):
             per_kernel[kname].append(ev[i].elapsed_time(ev[i + 1]))
-        step_ms.append(ev[0].elapsed_time(ev[len(kernels)]))
     avg = {kname: statistics.fmean(vals) for kname, vals in per_kernel.items()}
     med = {kname: statistics.median(vals) for kname, vals in per_kernel.items()}
-    ms_per_step = statistics.median(step_ms)
 
     f_fwd, f_bwd = flops(shape, True, False), flops(shape, False, True)
     fwd_ms = med["fwd"]
