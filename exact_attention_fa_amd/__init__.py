@@ -133,21 +133,22 @@ def _validate(*specs):
     shaped, typed, strided or host tensor would otherwise be read or written out of bounds.
     Each spec is (tensor, name, shape or None, numel or None, dtype or None); all tensors must
     share the first one's device."""
+    # (kept cheap: a latency-bound call spends more time here than in its kernels)
     for t, name, shape, numel, dtype in specs:
         if t is None:
             raise RuntimeError(f"{name} is required")
-        if shape is not None and tuple(t.shape) != tuple(shape):
+        if shape is not None and t.shape != tuple(shape):
             raise RuntimeError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
         if numel is not None and t.numel() != numel:
             raise RuntimeError(f"{name} has {t.numel()} elements, expected {numel}")
         if dtype is not None and t.dtype != dtype:
             raise RuntimeError(f"{name}: dtype mismatch, expected {dtype}, got {t.dtype}")
-    device = specs[0][0].device
+    index = specs[0][0].get_device()
     for t, name, *_ in specs:
         if not t.is_cuda:
             raise RuntimeError(f"{name} must live on the GPU")
-        if t.device != device:
-            raise RuntimeError(f"{name} is on {t.device}, expected {device}")
+        if t.get_device() != index:
+            raise RuntimeError(f"{name} is on {t.device}, expected {specs[0][0].device}")
         if not t.is_contiguous():
             raise RuntimeError(f"{name} must be contiguous")
 
