@@ -17,8 +17,8 @@ Prints ONE JSON line on stdout:
   hbm             the memory-bound stage (the backward preprocess): algorithmic bytes per
                   launch over its HIP-event time, against the HBM peak
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
-  kernel_*_ms     per-kernel average, median, minimum and maximum over K further steps timed
-                  kernel by kernel
+  kernel_*_ms     per-kernel average, median, minimum and maximum over the timed steps (steps
+                  under a millisecond: over K further steps timed kernel by kernel)
   mfma_util       MFMA (and VALU) busy fraction and sustained shader clock of the dominant
                   kernel, from the committed hardware-counter summary under profiles/ (null
                   when the kernel source has changed since the counters were taken)
@@ -30,10 +30,12 @@ Prints ONE JSON line on stdout:
                   the warmup and after the timed steps
 
 `value` and `ms_per_step` use the median of the per-step HIP-event durations (the pages'
-protocol: warmups, then the median of the timed repetitions; one event pair per step);
-`wall_ms_per_step` is the host wall time of the whole timed region divided by the steps.
-The per-kernel figures (kernel_*_ms, fwd/bwd TFLOP/s, roofline, hbm) come from K further
-steps, after the timed region, with an event between every two kernels.  The default workload is the
+protocol: warmups, then the median of the timed repetitions); `wall_ms_per_step` is the
+host wall time of the whole timed region divided by the steps.  Steps of a millisecond or
+more run the backward's stages with an event between every two kernels, which also gives
+the per-kernel figures; shorter steps (the tiny and grouped-query workloads) instead time one
+fa_fwd_splitkv and one fa_bwd call per step (one event pair) and take their per-kernel
+figures from K further steps.  The default workload is the
 long non-causal bf16 sequence (B=1, H=16, N=16384, D=128).  The tiny fp16 workloads
 (`--workload tiny_fp16_nc` / `tiny_fp16_causal`, B=1, H=2, N=256, D=64) are latency-bound:
 their line adds microseconds per kernel and the step's algorithmic HBM bytes per second.
@@ -560,28 +562,41 @@ def main():
     clock_before, power_before = gpu_clock(), gpu_power()
     for _ in range(args.warmup):
         step()
+    # the step's length, from three more (untimed) steps after the warmup
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(3):
+        step()
+    w1.record(stream)
     torch.cuda.synchronize()
+    short_step = w0.elapsed_time(w1) / 3 < 1.0  # milliseconds
 
-    # Timed region: exactly K steps, bracketed by device synchronisation, with one event pair
-    # per step (events between the kernels would add their own gaps to a latency-bound step).
-    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Timed region: exactly K steps, bracketed by device synchronisation.  Steps of a millisecond
+    # or more run kernel by kernel with an event between every two kernels (microseconds of
+    # events against milliseconds of work), so the per-kernel figures come from the same steps
+    # as the step time.  Shorter steps run as a caller runs them (one forward and one fa_bwd
+    # call, one event pair), since events and host calls between their kernels would be a
+    # visible part of their time; their per-kernel breakdown comes from K further steps.
+    latency_bound = name == "tiny_fp16"
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        sev[s][0].record(stream)
-        step()
-        sev[s][1].record(stream)
+        if short_step:
+            evs[s][0].record(stream)
+            step()
+            evs[s][len(kernels)].record(stream)
+        else:
+            step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     clock_after, power_after = gpu_clock(), gpu_power()
-    ms_per_step = statistics.median([a.elapsed_time(b) for a, b in sev])
-
-    # Per-kernel breakdown: K further steps through fa_bwd's stage entry points, with an event
-    # after every kernel.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
+    ms_per_step = statistics.median([ev[0].elapsed_time(ev[len(kernels)]) for ev in evs])
+    if short_step:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            step(evs[s])
+        torch.cuda.synchronize()
     per_kernel = {kname: [] for kname in kernels}
     for ev in evs:
         for i, kname in enumerate(kernels):
@@ -601,7 +616,6 @@ def main():
     kflops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.2 * f_bwd,
               "bwd_preprocess": 0.0, "bwd_postprocess": 0.0}
     kbytes = algorithmic_bytes(shape)
-    latency_bound = name == "tiny_fp16"
     if latency_bound:
         # A few hundred kilobytes per launch: every kernel is bound by launch and memory latency,
         # and the HBM rate of its algorithmic bytes is reported against the HBM peak.
