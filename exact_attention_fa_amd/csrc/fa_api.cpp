@@ -255,8 +255,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                                   causal, dtype, stream);
   FA_TRY(status_of(launch_bwd_preprocess(a)));
   FA_TRY(status_of(launch_bwd_dkdv(a)));
-  FA_TRY(status_of(launch_bwd_dq(a)));
-  return status_of(launch_bwd_postprocess(a));
+  return status_of(launch_bwd_dq_post(a));
 }
 
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace, size_t workspace_bytes,

@@ -468,6 +468,28 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
+// ---------------------------------------------------------------- dK/dV partial sums
+// dK/dV of KV head (b, hkv) = sum over its `grp` query heads of the fp32 partials
+// (dK partials already carry the softmax scale).  Item i covers 8 consecutive elements.
+template <typename TR>
+__device__ FA_INL void post_dkdv_item(long long i, const float* __restrict__ dKp, const float* __restrict__ dVp,
+                                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int grp,
+                                      long long head8) {
+  const long long bkv = i / head8, rem = i % head8;
+  f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka, va = ka, vb = ka;
+  for (int h = 0; h < grp; ++h) {
+    const long long src = ((bkv * grp + h) * head8 + rem) * 8;
+    ka += *reinterpret_cast<const f32x4*>(dKp + src);
+    kb += *reinterpret_cast<const f32x4*>(dKp + src + 4);
+    va += *reinterpret_cast<const f32x4*>(dVp + src);
+    vb += *reinterpret_cast<const f32x4*>(dVp + src + 4);
+  }
+  *reinterpret_cast<u32x4*>(dK + i * 8) =
+      u32x4{TR::pack(ka[0], ka[1]), TR::pack(ka[2], ka[3]), TR::pack(kb[0], kb[1]), TR::pack(kb[2], kb[3])};
+  *reinterpret_cast<u32x4*>(dV + i * 8) =
+      u32x4{TR::pack(va[0], va[1]), TR::pack(va[2], va[3]), TR::pack(vb[0], vb[1]), TR::pack(vb[2], vb[3])};
+}
+
 // ---------------------------------------------------------------- dQ
 // Query-stationary: a workgroup owns 128 or 256 query rows (32 per wave) of one head and streams
 // 32-key tiles of K and V of its KV head through LDS (direct loads issued three tiles ahead;
@@ -485,14 +507,20 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // end (one fixed-order addition, still deterministic).
 // PART: small grids also cut each query tile's key range into n_kp pieces, one workgroup
 // each; a piece writes its unscaled fp32 dQ partial (dQp) and bwd_dq_sum_kernel adds them.
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART>
+// SUMS: the workgroups also run the grouped-query dK/dV partial sums (post_dkdv_item) after
+// their own dQ rows, each an interval of the n8post items: on a one-round causal grid weighted
+// by n_qt - qt towards the light tiles, which finish early, else equal.  (fa_bwd uses this in
+// place of the separate postprocess launch where the grid has no key-range pieces.)
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART, bool SUMS>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
               int Hq, int Hkv, int N, int n_qt, float c2, float scale, uint32_t qsign, int snake, int n_kp,
-              float* __restrict__ dQp) {
+              float* __restrict__ dQp, const float* __restrict__ dKp, const float* __restrict__ dVp,
+              uint16_t* __restrict__ dKo, uint16_t* __restrict__ dVo, int pgrp, long long head8, long long n8post) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
+  static_assert(!(SUMS && PART), "the fused partial sums run on grids without key-range pieces");
   constexpr int GW = NW / SPLIT;            // waves per group
   constexpr int BR = GW * 32, BC = kDqBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps over the head dim
@@ -826,11 +854,30 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     stage_row<HDP>(qs, c, g, reinterpret_cast<const u32x2(&)[HDP / 32][4]>(w[p * (DB / PASSES)]));
     store_staged<HDP * 2, 32, HD * 2>(qs, dQ + ((size_t)bh * N + qw0) * HD + p * HDP, N - qw0, lane);
   }
+
+  if constexpr (SUMS) {
+    constexpr int NT = (SPLIT == 2 ? GW : NW) * 64;  // the threads still here (group 1 has left)
+    const long long heads = gridDim.x / n_qt;      // B * Hq
+    long long lo, hi;
+    if (CAUSAL && snake) {
+      // weights n_qt - t for tile t of every head, in (head, tile) order
+      const long long wh = (long long)n_qt * (n_qt + 1) / 2;
+      const long long pre = (long long)bh * wh + (long long)qt * n_qt - (long long)qt * (qt - 1) / 2;
+      const long long tot = heads * wh;
+      lo = n8post * pre / tot;
+      hi = n8post * (pre + n_qt - qt) / tot;
+    } else {
+      const long long j = (long long)bh * n_qt + qt;
+      lo = n8post * j / gridDim.x;
+      hi = n8post * (j + 1) / gridDim.x;
+    }
+    for (long long i = lo + tid; i < hi; i += NT) post_dkdv_item<TR>(i, dKp, dVp, dKo, dVo, pgrp, head8);
+  }
 }
 
 // ---------------------------------------------------------------- postprocess
-// dK/dV of KV head (b, hkv) = sum over its `grp` query heads of the fp32 partials
-// (dK partials already carry the softmax scale).
+// dK/dV of KV head (b, hkv) = sum over its `grp` query heads of the fp32 partials, one
+// item per thread (post_dkdv_item).
 template <typename TR>
 __global__ void __launch_bounds__(kThreads)
 bwd_post_dkdv_kernel(const float* __restrict__ dKp, const float* __restrict__ dVp,
@@ -838,19 +885,7 @@ bwd_post_dkdv_kernel(const float* __restrict__ dKp, const float* __restrict__ dV
                      long long head8, long long n8) {
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n8) return;
-  const long long bkv = i / head8, rem = i % head8;
-  f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka, va = ka, vb = ka;
-  for (int h = 0; h < grp; ++h) {
-    const long long src = ((bkv * grp + h) * head8 + rem) * 8;
-    ka += *reinterpret_cast<const f32x4*>(dKp + src);
-    kb += *reinterpret_cast<const f32x4*>(dKp + src + 4);
-    va += *reinterpret_cast<const f32x4*>(dVp + src);
-    vb += *reinterpret_cast<const f32x4*>(dVp + src + 4);
-  }
-  *reinterpret_cast<u32x4*>(dK + i * 8) =
-      u32x4{TR::pack(ka[0], ka[1]), TR::pack(ka[2], ka[3]), TR::pack(kb[0], kb[1]), TR::pack(kb[2], kb[3])};
-  *reinterpret_cast<u32x4*>(dV + i * 8) =
-      u32x4{TR::pack(va[0], va[1]), TR::pack(va[2], va[3]), TR::pack(vb[0], vb[1]), TR::pack(vb[2], vb[3])};
+  post_dkdv_item<TR>(i, dKp, dVp, dK, dV, grp, head8);
 }
 
 // dQ of row (bh, n) = scale * the sum, in piece order, of its n_kp fp32 partials.
@@ -924,7 +959,7 @@ hipError_t dkdv_hd(const BwdArgs& a) {
   return partial ? dkdv_t<TR, HD, false, true>(a) : dkdv_t<TR, HD, false, false>(a);
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false, bool POST = false>
 hipError_t dq_nw(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
   constexpr int BR = NW / SPLIT * 32;
@@ -932,12 +967,18 @@ hipError_t dq_nw(const BwdArgs& a) {
   const int n_kp = PART ? w.n_kp : 1;
   const long long blocks = a.B * a.Hq * (long long)n_qt * n_kp;
   float* const dqp = PART ? reinterpret_cast<float*>(a.ws + w.dq_part) : nullptr;
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT, PART>), dim3((unsigned)blocks), dim3(NW * 64), 0, a.stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+  // (POST: the grouped-query dK/dV partial sums ride along, as in post_t)
+  const long long kv8 = POST ? a.B * a.Hkv * a.N * a.D / 8 : 0;
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT, PART, POST>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                     a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
                      static_cast<uint16_t*>(a.dq), (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, exp2_factor(a.scale),
-                     a.scale, sign_bits(a.scale), (int)grid_fits(blocks, 8 / NW), n_kp, dqp);
+                     a.scale, sign_bits(a.scale), (int)grid_fits(blocks, 8 / NW), n_kp, dqp,
+                     POST ? reinterpret_cast<const float*>(a.ws + w.dk_part) : nullptr,
+                     POST ? reinterpret_cast<const float*>(a.ws + w.dv_part) : nullptr,
+                     POST ? static_cast<uint16_t*>(a.dk) : nullptr, POST ? static_cast<uint16_t*>(a.dv) : nullptr,
+                     (int)(a.Hq / a.Hkv) * w.n_qp, a.N * a.D / 8, kv8);
   if constexpr (PART) {
     FA_HIP_TRY(hipGetLastError());
     const long long n8 = a.B * a.Hq * a.N * a.D / 8;
@@ -952,20 +993,24 @@ hipError_t dq_nw(const BwdArgs& a) {
 // small to split over 8 waves.  Smaller grids use 128-query tiles: 8-wave workgroups that split
 // the key range over two wave groups (causal grids, whose tiles carry uneven work, and grids
 // too small to give every CU two 4-wave workgroups), else 4-wave workgroups, two per CU.
+// With `post` (fa_bwd, when the dK/dV pass wrote partials) the pass also runs their sums
+// unless its grid takes key-range pieces; *fused says whether it did.
 template <typename TR, int HD, bool CAUSAL>
-hipError_t dq_t(const BwdArgs& a) {
+hipError_t dq_t(const BwdArgs& a, bool post, bool* fused) {
   const long long big = a.B * a.Hq * ((a.N + 255) / 256);
+  *fused = post && bwd_key_pieces(a.B, a.Hq, a.N, a.D) == 1;
   if constexpr (HD == 128)
-    if (big >= 512) return dq_nw<TR, HD, CAUSAL, 8, 1>(a);
+    if (big >= 512) return *fused ? dq_nw<TR, HD, CAUSAL, 8, 1, false, true>(a) : dq_nw<TR, HD, CAUSAL, 8, 1>(a);
   if (bwd_key_pieces(a.B, a.Hq, a.N, a.D) > 1) return dq_nw<TR, HD, CAUSAL, 8, 2, true>(a);
-  if (a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512) return dq_nw<TR, HD, CAUSAL, 8, 2>(a);
-  return dq_nw<TR, HD, CAUSAL, 4, 1>(a);
+  if (a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512)
+    return *fused ? dq_nw<TR, HD, CAUSAL, 8, 2, false, true>(a) : dq_nw<TR, HD, CAUSAL, 8, 2>(a);
+  return *fused ? dq_nw<TR, HD, CAUSAL, 4, 1, false, true>(a) : dq_nw<TR, HD, CAUSAL, 4, 1>(a);
 }
 
 template <typename TR>
-hipError_t dq_dt(const BwdArgs& a) {
-  if (a.D == 64) return a.causal ? dq_t<TR, 64, true>(a) : dq_t<TR, 64, false>(a);
-  return a.causal ? dq_t<TR, 128, true>(a) : dq_t<TR, 128, false>(a);
+hipError_t dq_dt(const BwdArgs& a, bool post, bool* fused) {
+  if (a.D == 64) return a.causal ? dq_t<TR, 64, true>(a, post, fused) : dq_t<TR, 64, false>(a, post, fused);
+  return a.causal ? dq_t<TR, 128, true>(a, post, fused) : dq_t<TR, 128, false>(a, post, fused);
 }
 
 template <typename TR>
@@ -1024,7 +1069,19 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a) {
   if (a.f32) return launch_bwd_dq_f32(a);
-  return a.bf16 ? dq_dt<Bf16>(a) : dq_dt<F16>(a);
+  bool fused = false;
+  return a.bf16 ? dq_dt<Bf16>(a, false, &fused) : dq_dt<F16>(a, false, &fused);
+}
+
+hipError_t launch_bwd_dq_post(const BwdArgs& a) {
+  if (a.f32) {
+    FA_HIP_TRY(launch_bwd_dq_f32(a));
+    return launch_bwd_postprocess(a);
+  }
+  const bool partial = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D).partial_dkdv;
+  bool fused = false;
+  FA_HIP_TRY(a.bf16 ? dq_dt<Bf16>(a, partial, &fused) : dq_dt<F16>(a, partial, &fused));
+  return fused ? hipSuccess : launch_bwd_postprocess(a);
 }
 
 hipError_t launch_bwd_postprocess(const BwdArgs& a) {

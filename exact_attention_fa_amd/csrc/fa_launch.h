@@ -79,6 +79,9 @@ int fwd_auto_parts(long long B, long long Hq, long long N, long long D, bool cau
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
+// The dQ pass followed by the postprocess, with the grouped-query dK/dV partial sums run inside
+// the dQ pass where its grid allows: the same results as launch_bwd_dq, launch_bwd_postprocess.
+hipError_t launch_bwd_dq_post(const BwdArgs& a);
 hipError_t launch_bwd_postprocess(const BwdArgs& a);
 // The fp32 verification path (fa_f32.hip); launch_fwd and the launch_bwd_* stages dispatch to
 // these when FwdArgs::f32 / BwdArgs::f32 is set.

@@ -167,20 +167,31 @@ def test_backward_bitwise_deterministic(torch_fa, causal):
         assert torch.equal(a, b)
 
 
-def test_backward_stages_equal_fused_call(torch_fa):
-    """The exported stages, run in order on one stream, reproduce fa_bwd bit for bit."""
+STAGE_SHAPES = [
+    (2, 8, 4, 700, 64, "fp16", True),      # dQ key-range pieces: separate partial sums
+    (1, 16, 4, 2048, 128, "fp16", True),   # one-round causal grid: the dQ pass runs the sums
+    (2, 16, 4, 4096, 128, "bf16", False),  # 256-query dQ workgroups with the sums
+]
+
+
+@pytest.mark.parametrize("dims", STAGE_SHAPES, ids=[f"B{b}H{hq}/{hk}N{n}D{d}{t}{'c' if cz else ''}"
+                                                    for b, hq, hk, n, d, t, cz in STAGE_SHAPES])
+def test_backward_stages_equal_fused_call(torch_fa, dims):
+    """The exported stages, run in order on one stream, reproduce fa_bwd bit for bit (fa_bwd
+    runs the grouped-query partial sums inside its dQ pass where the grid allows)."""
     torch, fa = torch_fa
     from exact_attention_fa_amd.inputs import Shape
-    shape = Shape(2, 8, 4, 700, 64, "fp16", True)
+    shape = Shape(*dims)
+    B, Hq, Hkv, N, D, causal = shape.B, shape.Hq, shape.Hkv, shape.N, shape.D, shape.causal
     q, k, v, do = inputs(shape, 23)
-    o, lse = fa.fa_fwd(q, k, v, causal=True)
-    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=True)
-    ws = torch.empty(fa.fa_bwd_workspace_size(2, 8, 4, 700, 64), dtype=torch.uint8, device="cuda")
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D), dtype=torch.uint8, device="cuda")
     dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
-    fa.fa_bwd_preprocess(o, do, lse, ws, 4)
-    fa.fa_bwd_dkdv(q, k, v, do, dk2, dv2, ws, causal=True)
-    fa.fa_bwd_dq(q, k, v, do, dq2, ws, causal=True)
-    fa.fa_bwd_postprocess(dk2, dv2, ws, 8)
+    fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
+    fa.fa_bwd_dkdv(q, k, v, do, dk2, dv2, ws, causal=causal)
+    fa.fa_bwd_dq(q, k, v, do, dq2, ws, causal=causal)
+    fa.fa_bwd_postprocess(dk2, dv2, ws, Hq)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
