@@ -171,6 +171,7 @@ STAGE_SHAPES = [
     (2, 8, 4, 700, 64, "fp16", True),      # dQ key-range pieces: separate partial sums
     (1, 16, 4, 2048, 128, "fp16", True),   # one-round causal grid: the dQ pass runs the sums
     (2, 16, 4, 4096, 128, "bf16", False),  # 256-query dQ workgroups with the sums
+    (2, 16, 4, 4096, 64, "fp16", False),   # 4-wave dQ workgroups (two per CU) with the sums
 ]
 
 
