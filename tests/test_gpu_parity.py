@@ -267,11 +267,11 @@ def test_shard_causal_bf16_full():
     log("  errors", errs)
 
 
-def _random_cases(n, seed):
+def _random_cases(n, seed, n_max=1500, cap=4e7):
     """Seeded shapes across the supported space: batch, MQA/GQA/MHA head ratios, ragged N
-    (log-uniform up to ~1500, including 1), both head dims and dtypes, causal or not, and the
+    (log-uniform up to n_max, including 1), both head dims and dtypes, causal or not, and the
     default, zero, small, large or negative softmax scales.  Each case's oracle work is capped
-    (B * Hq * N^2 <= 4e7) so the whole sweep runs in well under a minute."""
+    (B * Hq * N^2 <= cap) so the whole sweep runs in well under a minute."""
     import numpy as np
     rng = np.random.default_rng(seed)
     cases = []
@@ -279,19 +279,19 @@ def _random_cases(n, seed):
         B = int(rng.integers(1, 4))
         Hkv = int(rng.choice([1, 1, 2, 3]))
         grp = int(rng.choice([1, 1, 2, 3, 4, 8]))
-        N = int(np.clip(round(float(np.exp(rng.uniform(0.0, np.log(1500))))), 1, 1500))
+        N = int(np.clip(round(float(np.exp(rng.uniform(0.0, np.log(n_max))))), 1, n_max))
         D = int(rng.choice([64, 128]))
         dtype = str(rng.choice(["bf16", "fp16"]))
         causal = bool(rng.integers(0, 2))
         kind = int(rng.integers(0, 5))
         scale = None if kind < 2 else (0.0 if kind == 2 else float(np.round(rng.uniform(-0.25, 0.25), 4)))
-        if B * Hkv * grp * N * N > 4e7:
+        if B * Hkv * grp * N * N > cap:
             continue
         cases.append((B, Hkv * grp, Hkv, N, D, dtype, causal, scale))
     return cases
 
 
-RANDOM = _random_cases(64, 2026)
+RANDOM = _random_cases(64, 2026) + _random_cases(16, 2027, n_max=4000, cap=2e8)
 
 
 @pytest.mark.parametrize("dims", RANDOM, ids=[f"B{b}H{hq}/{hk}N{n}D{d}{t}{'c' if cz else ''}s{sc}"
