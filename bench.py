@@ -3,8 +3,9 @@
 
 A step is one pass of the whole path over one batch of synthetic input: the forward
 (fa_fwd_splitkv with the library's choice of key-range pieces, which is exactly fa_fwd
-except on grids too small to fill the GPU) and the backward (fa_bwd: preprocess, dK/dV pass,
-dQ pass, postprocess) on the same stream.
+except on grids too small to fill the GPU) and the backward (fa_bwd, in the stage order
+fa_bwd_plan names: the dQ pass forming the row values, then the dK/dV pass; or the
+preprocess, the dK/dV pass, the dQ pass and the postprocess) on the same stream.
 Inputs, outputs and workspace are allocated and resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout:
@@ -14,8 +15,12 @@ Prints ONE JSON line on stdout:
                   on the stream it is launched on, against the MFMA peak; `traffic` is its HBM
                   bytes per launch from the committed hardware-counter summary under profiles/,
                   or null when the kernel source has changed since the counters were taken
-  hbm             the memory-bound stage (the backward preprocess): algorithmic bytes per
-                  launch over its HIP-event time, against the HBM peak
+  hbm             the memory-bound stage, the backward preprocess (fa_bwd_preprocess), timed
+                  on its own after the steps: an event pair around each of 10 launches over
+                  rotated copies of O and dO (at least 1 GiB in all, more than the Infinity
+                  Cache holds); algorithmic bytes per launch over the median, against the HBM
+                  peak (where fa_bwd forms these values inside its dQ pass, the stage is not
+                  part of the step)
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
   kernel_*_ms     per-kernel average, median, minimum and maximum over the timed steps (steps
                   under a millisecond: over K further steps timed kernel by kernel)
@@ -32,8 +37,8 @@ Prints ONE JSON line on stdout:
 `value` and `ms_per_step` use the median of the per-step HIP-event durations (the pages'
 protocol: warmups, then the median of the timed repetitions); `wall_ms_per_step` is the
 host wall time of the whole timed region divided by the steps.  Steps of a millisecond or
-more run the backward's stages with an event between every two kernels, which also gives
-the per-kernel figures; shorter steps (the tiny and grouped-query workloads) instead time one
+more run the backward's stages (in fa_bwd's order, the same launches) with an event between
+every two kernels, which also gives the per-kernel figures; shorter steps (the tiny and grouped-query workloads) instead time one
 fa_fwd_splitkv and one fa_bwd call per step (one event pair) and take their per-kernel
 figures from K further steps.  The default workload is the
 long non-causal bf16 sequence (B=1, H=16, N=16384, D=128).  The tiny fp16 workloads
@@ -310,21 +315,49 @@ def cpu_baseline(shape, seed, budget_s):
     }
 
 
-def algorithmic_bytes(shape):
+def algorithmic_bytes(shape, rows_first=False):
     """Algorithmic HBM bytes of each timed stage: every input read once and every output
     written once (K/V re-reads across query tiles and Q/dO re-reads across key blocks are
-    implementation traffic, not counted)."""
+    implementation traffic, not counted).  rows_first: the dQ pass forms the row values
+    (fa_bwd_dq_rows) and the preprocess stage is not run."""
     es = 2 if shape.dtype in ("bf16", "fp16") else 4
     q = shape.B * shape.Hq * shape.N * shape.D * es
     kv = shape.B * shape.Hkv * shape.N * shape.D * es
     rows = shape.B * shape.Hq * shape.N
-    return {
+    out = {
         "fwd": 2 * q + 2 * kv + 4 * rows,                    # Q, K, V read; O, LSE written
         "bwd_preprocess": 2 * q + 4 * rows + 8 * rows,       # O, dO, LSE read; -D, LSE*log2 e written
         "bwd_dkdv": 2 * q + 2 * kv + 8 * rows + 2 * kv,      # Q, dO, K, V, LSE, D read; dK, dV written
         "bwd_dq": 2 * q + 2 * kv + 8 * rows + q,             # Q, dO, K, V, LSE, D read; dQ written
         "bwd_postprocess": 0,                                # partials only (none for MHA grids)
     }
+    if rows_first:
+        # Q, dO, O, K, V, LSE read; -D, LSE*log2 e and dQ written
+        out["bwd_dq"] = 3 * q + 2 * kv + 4 * rows + 8 * rows + q
+        del out["bwd_preprocess"], out["bwd_postprocess"]
+    return out
+
+
+def standalone_preprocess(fa, torch, o, do, lse, ws, Hkv, launches=10):
+    """Median time (ms) of one fa_bwd_preprocess launch, timed with an event pair around each of
+    `launches` launches over rotated copies of O and dO: enough copies for 1 GiB of inputs
+    (at least two), so that no launch finds its inputs in the 256 MB Infinity Cache."""
+    import statistics
+    copies = max(2, min(16, -(-(1 << 30) // max(1, 2 * o.numel() * o.element_size()))))
+    pairs = [(o.clone(), do.clone()) for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+    for oc, dc in pairs:
+        fa.fa_bwd_preprocess(oc, dc, lse, ws, Hkv)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for i, (a, b) in enumerate(ev):
+        oc, dc = pairs[i % copies]
+        a.record(stream)
+        fa.fa_bwd_preprocess(oc, dc, lse, ws, Hkv)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+    del pairs
+    return ms, copies
 
 
 def counter_summary(kernel, workload):
@@ -393,11 +426,21 @@ def _counter_avg(directory, counter):
     return {k: statistics.fmean(v) for k, v in vals.items()}
 
 
+def rows_first_plan(shape):
+    """True where fa_bwd runs the dQ pass first and forms the row values there
+    (fa_bwd_plan == FA_BWD_PLAN_ROWS); asks the library, which needs no GPU for it."""
+    import exact_attention_fa_amd as fa
+    code = {"fp16": fa.FA_FP16, "bf16": fa.FA_BF16}[shape.dtype]
+    return fa.fa_bwd_plan(shape.B, shape.Hq, shape.Hkv, shape.N, shape.D, code) == fa.FA_BWD_PLAN_ROWS
+
+
 def _traffic(dirs, copy_bytes, workload):
-    """The blocks that profiles/traffic_<stage>_<workload>.txt hold (see summarize)."""
+    """The blocks that profiles/traffic_<stage>_<workload>.txt hold (see summarize).  The
+    preprocess's launches in these runs are the standalone ones after the steps."""
     from exact_attention_fa_amd.inputs import WORKLOADS
     name, variant = WORKLOAD_KEYS[workload]
-    alg = algorithmic_bytes(WORKLOADS[name][variant])
+    shape = WORKLOADS[name][variant]
+    alg = {**algorithmic_bytes(shape), **algorithmic_bytes(shape, rows_first_plan(shape))}
     fetch, write = _counter_avg(dirs[0], "FETCH_SIZE"), _counter_avg(dirs[1], "WRITE_SIZE")
     cfetch, cwrite = _counter_avg(dirs[2], "FETCH_SIZE"), _counter_avg(dirs[3], "WRITE_SIZE")
     copy = [k for k in cfetch if "copy" in k.lower()]
@@ -537,27 +580,37 @@ def main():
                       device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_postprocess"]
+    # fa_bwd's stages in its own order: the dQ pass forming the row values, then the dK/dV pass
+    # (FA_BWD_PLAN_ROWS), or the preprocess, dK/dV pass, dQ pass and postprocess
+    rows_first = rows_first_plan(shape)
+    if rows_first:
+        kernels = ["fwd", "bwd_dq", "bwd_dkdv"]
+    else:
+        kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_postprocess"]
+
+    def fwd_call():
+        fa.fa_fwd_splitkv(q, k, v, causal=causal, softmax_scale=scale, n_split=n_split, workspace=fws, out=o, lse=lse)
+
+    calls = {
+        "fwd": fwd_call,
+        "bwd_preprocess": lambda: fa.fa_bwd_preprocess(o, do, lse, ws, Hkv),
+        "bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=causal, softmax_scale=scale),
+        "bwd_dq": ((lambda: fa.fa_bwd_dq_rows(q, k, v, o, do, lse, dq, ws, causal=causal, softmax_scale=scale))
+                   if rows_first else
+                   (lambda: fa.fa_bwd_dq(q, k, v, do, dq, ws, causal=causal, softmax_scale=scale))),
+        "bwd_postprocess": lambda: fa.fa_bwd_postprocess(dk, dv, ws, Hq),
+    }
 
     def step(ev=None):
         if ev is None:  # as a caller runs it: one forward call and one fa_bwd call
-            fa.fa_fwd_splitkv(q, k, v, causal=causal, softmax_scale=scale, n_split=n_split, workspace=fws, out=o,
-                              lse=lse)
+            fwd_call()
             fa.fa_bwd(q, k, v, o, do, lse, causal=causal, softmax_scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
             return
         # kernel by kernel: fa_bwd's stages (the same launches) with an event between every two
-        ev[0].record(stream)
-        fa.fa_fwd_splitkv(q, k, v, causal=causal, softmax_scale=scale, n_split=n_split, workspace=fws, out=o,
-                          lse=lse)
-        ev[1].record(stream)
-        fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
-        ev[2].record(stream)
-        fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=causal, softmax_scale=scale)
-        ev[3].record(stream)
-        fa.fa_bwd_dq(q, k, v, do, dq, ws, causal=causal, softmax_scale=scale)
-        ev[4].record(stream)
-        fa.fa_bwd_postprocess(dk, dv, ws, Hq)
-        ev[5].record(stream)
+        for i, kname in enumerate(kernels):
+            ev[i].record(stream)
+            calls[kname]()
+        ev[len(kernels)].record(stream)
 
     clock_before, power_before = gpu_clock(), gpu_power()
     for _ in range(args.warmup):
@@ -615,7 +668,7 @@ def main():
     # (another 0.4 of the backward's FLOPs) is work this design adds, so it is not credited.
     kflops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.2 * f_bwd,
               "bwd_preprocess": 0.0, "bwd_postprocess": 0.0}
-    kbytes = algorithmic_bytes(shape)
+    kbytes = algorithmic_bytes(shape, rows_first)
     if latency_bound:
         # A few hundred kilobytes per launch: every kernel is bound by launch and memory latency,
         # and the HBM rate of its algorithmic bytes is reported against the HBM peak.
@@ -630,11 +683,13 @@ def main():
                     "traffic": measured_traffic(dominant, args.workload), "avg_ms": round(avg[dominant], 4)}
     # The memory-bound stage: the preprocess reads O and dO (input dtype) and the LSE, and
     # writes -D and LSE*log2(e), all fp32 per row.
-    pre_bytes = kbytes["bwd_preprocess"]
-    pre_gbs = pre_bytes / (avg["bwd_preprocess"] * 1e-3) / 1e9
+    pre_bytes = algorithmic_bytes(shape)["bwd_preprocess"]
+    pre_ms, pre_copies = standalone_preprocess(fa, torch, o, do, lse, ws, Hkv)
+    pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
     hbm = {"kernel": "bwd_preprocess", "bound": "hbm", "achieved": round(pre_gbs, 1), "peak": PEAK_HBM_GBS,
            "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": pre_bytes,
-           "avg_ms": round(avg["bwd_preprocess"], 4)}
+           "median_ms": round(pre_ms, 4), "timed": f"alone after the steps, {pre_copies} rotated copies of O and dO",
+           "in_step": not rows_first}
 
     out = {
         "metric": METRIC,

@@ -23,7 +23,8 @@ import threading
 
 __all__ = [
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_size",
-    "fa_merge_partials", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_postprocess",
+    "fa_merge_partials", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_rows",
+    "fa_bwd_postprocess", "fa_bwd_plan", "FA_BWD_PLAN_STAGES", "FA_BWD_PLAN_ROWS",
     "fa_bwd_workspace_size", "fa_version", "fa_status_string", "library_path", "load_library",
     "EXPORTED_SYMBOLS", "FA_FP16", "FA_BF16", "FA_FP32", "fa_bwd_noalloc", "FA_NOALLOC_SCRATCH_BYTES",
 ]
@@ -31,6 +32,8 @@ __all__ = [
 FA_FP16 = 0
 FA_BF16 = 1
 FA_FP32 = 2
+FA_BWD_PLAN_STAGES = 0  # fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_postprocess
+FA_BWD_PLAN_ROWS = 1    # fa_bwd_dq_rows, fa_bwd_dkdv
 _LIB_NAME = "libfa_mi355x.so"
 _lock = threading.Lock()
 _lib = None
@@ -60,6 +63,10 @@ _SIGS = {
     "fa_bwd_dq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                    _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
                   ctypes.c_int),
+    "fa_bwd_dq_rows": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                        _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp],
+                       ctypes.c_int),
+    "fa_bwd_plan": ([_i64, _i64, _i64, _i64, _i64, ctypes.c_int], ctypes.c_int),
     "fa_bwd_postprocess": ([_vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64,
                             ctypes.c_int, _vp], ctypes.c_int),
     "fa_bwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -334,6 +341,30 @@ def fa_bwd_dq(q, k, v, do, dq, workspace, causal=False, softmax_scale=None):
                                   _nbytes(workspace), B, Hq, Hkv, N, D, _scale(D, softmax_scale),
                                   int(bool(causal)), _dtype_code(q), _stream(q))
     _check(rc, "fa_bwd_dq")
+
+
+def fa_bwd_dq_rows(q, k, v, o, do, lse, dq, workspace, causal=False, softmax_scale=None):
+    """fa_bwd_preprocess and fa_bwd_dq as one pass (the row values are formed where the dQ pass
+    holds each row, and stored in the workspace for fa_bwd_dkdv)."""
+    import torch
+    B, Hq, Hkv, N, D = _dims(q, k, v)
+    _dtype_code(q)
+    _validate(*_qkv_specs(q, k, v), (o, "o", q.shape, None, q.dtype), (do, "do", q.shape, None, q.dtype),
+              (lse, "lse", (B, Hq, N), None, torch.float32), (dq, "dq", q.shape, None, q.dtype),
+              (workspace, "workspace", None, None, None))
+    rc = load_library().fa_bwd_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                       _ptr(workspace), _nbytes(workspace), B, Hq, Hkv, N, D,
+                                       _scale(D, softmax_scale), int(bool(causal)), _dtype_code(q), _stream(q))
+    _check(rc, "fa_bwd_dq_rows")
+
+
+def fa_bwd_plan(B: int, Hq: int, Hkv: int, N: int, D: int, dtype: int) -> int:
+    """The stage order fa_bwd enqueues: FA_BWD_PLAN_ROWS (fa_bwd_dq_rows, fa_bwd_dkdv) or
+    FA_BWD_PLAN_STAGES (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_postprocess)."""
+    rc = load_library().fa_bwd_plan(B, Hq, Hkv, N, D, dtype)
+    if rc < 0:
+        _check(-rc, "fa_bwd_plan")
+    return rc
 
 
 def fa_bwd_postprocess(dk, dv, workspace, Hq: int):

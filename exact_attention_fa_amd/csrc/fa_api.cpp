@@ -113,6 +113,12 @@ int check_bwd_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, i
   return FA_OK;
 }
 
+// fa_bwd's order: the dQ pass first, forming the row values itself, where the dK/dV pass writes
+// dk and dv directly (16-bit tensors); otherwise the preprocess first.
+bool bwd_rows_first(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype) {
+  return dtype != FA_FP32 && !bwd_workspace_layout(B, Hq, Hkv, N, D).partial_dkdv;
+}
+
 BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, void* ws, int64_t B, int64_t Hq,
                       int64_t Hkv, int64_t N, int64_t D, float scale, int causal, int dtype, void* stream) {
@@ -253,6 +259,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   FA_TRY(check_alias(r, 10));
   const BwdArgs a = make_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, D, softmax_scale,
                                   causal, dtype, stream);
+  // Without dK/dV partials the dQ pass runs first and forms the row values the dK/dV pass reads
+  // (one launch fewer); otherwise the preprocess runs first and the dQ pass follows the dK/dV
+  // pass, whose partials it sums.
+  if (bwd_rows_first(B, Hq, Hkv, N, D, dtype)) {
+    FA_TRY(status_of(launch_bwd_dq_rows(a)));
+    return status_of(launch_bwd_dkdv(a));
+  }
   FA_TRY(status_of(launch_bwd_preprocess(a)));
   FA_TRY(status_of(launch_bwd_dkdv(a)));
   return status_of(launch_bwd_dq_post(a));
@@ -311,6 +324,34 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
   const BwdArgs a = make_bwd_args(q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, D,
                                   softmax_scale, causal, dtype, stream);
   return status_of(launch_bwd_dq(a));
+}
+
+int fa_bwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype) {
+  const int e = check_dtype(dtype) != FA_OK ? check_dtype(dtype) : check_dims(B, Hq, Hkv, N, D);
+  if (e != FA_OK) return -e;
+  return bwd_rows_first(B, Hq, Hkv, N, D, dtype) ? FA_BWD_PLAN_ROWS : FA_BWD_PLAN_STAGES;
+}
+
+int fa_bwd_dq_rows(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t N, int64_t D, float softmax_scale, int causal, int dtype, void* stream) {
+  FA_TRY(check_bwd_common(B, Hq, Hkv, N, D, dtype, workspace, workspace_bytes));
+  FA_TRY(check_scale(softmax_scale));
+  const void* p16[] = {q, k, v, o, dout, dq};
+  for (const void* p : p16) FA_TRY(check_ptr(p, 16));
+  FA_TRY(check_ptr(lse, 4));
+  const size_t qb = (size_t)(B * Hq * N * D) * elem_size(dtype), kb = (size_t)(B * Hkv * N * D) * elem_size(dtype);
+  const Range r[] = {{q, qb, false},    {k, kb, false},  {v, kb, false},
+                     {o, qb, false},    {dout, qb, false}, {lse, (size_t)(B * Hq * N) * 4, false},
+                     {dq, qb, true},    {workspace, bwd_workspace_layout(B, Hq, Hkv, N, D).total, true}};
+  FA_TRY(check_alias(r, 8));
+  const BwdArgs a = make_bwd_args(q, k, v, o, dout, lse, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, D,
+                                  softmax_scale, causal, dtype, stream);
+  if (a.f32) {  // the fp32 path has no combined pass: the two stages
+    FA_TRY(status_of(launch_bwd_preprocess(a)));
+    return status_of(launch_bwd_dq(a));
+  }
+  return status_of(launch_bwd_dq_rows(a));
 }
 
 int fa_bwd_postprocess(void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq,

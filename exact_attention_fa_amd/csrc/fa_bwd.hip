@@ -511,16 +511,24 @@ __device__ FA_INL void post_dkdv_item(long long i, const float* __restrict__ dKp
 // their own dQ rows, each an interval of the n8post items: on a one-round causal grid weighted
 // by n_qt - qt towards the light tiles, which finish early, else equal.  (fa_bwd uses this in
 // place of the separate postprocess launch where the grid has no key-range pieces.)
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART, bool SUMS>
+// ROWS: the pass forms its rows' D and LSE*log2(e) itself, from O, dO and the LSE, and stores
+// them (-D and LSE*log2(e)) for the dK/dV pass that follows it, in place of the preprocess
+// launch.  The sum runs in the preprocess kernel's order (the same per-16-byte FMA chains, the
+// same pairwise tree), so both routes give the same bits.  (fa_bwd runs the dQ pass first this
+// way wherever the dK/dV pass writes no partials.)
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART, bool SUMS, bool ROWS>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ L2, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
               int Hq, int Hkv, int N, int n_qt, float c2, float scale, uint32_t qsign, int snake, int n_kp,
               float* __restrict__ dQp, const float* __restrict__ dKp, const float* __restrict__ dVp,
-              uint16_t* __restrict__ dKo, uint16_t* __restrict__ dVo, int pgrp, long long head8, long long n8post) {
+              uint16_t* __restrict__ dKo, uint16_t* __restrict__ dVo, int pgrp, long long head8, long long n8post,
+              const uint16_t* __restrict__ Oin, const float* __restrict__ LSEin, float* __restrict__ L2o,
+              float* __restrict__ Dlo) {
   static_assert(SPLIT == 1 || SPLIT == 2, "one or two groups");
   static_assert(!(SUMS && PART), "the fused partial sums run on grids without key-range pieces");
+  static_assert(!(SUMS && ROWS), "the partial sums follow a dK/dV pass, the row values precede one");
   constexpr int GW = NW / SPLIT;            // waves per group
   constexpr int BR = GW * 32, BC = kDqBC;  // query rows per workgroup (32 per wave), keys per tile
   constexpr int KST = HD / 16;              // k-steps over the head dim
@@ -607,8 +615,43 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     qf[kk] = ld16_if(Q + rowoff + kk * 16 + g * 8, qi < N) ^ qsign;  // -Q for a negative scale
     of[kk] = ld16_if(dO + rowoff + kk * 16 + g * 8, qi < N);
   }
-  const float l2 = qi < N ? L2[(size_t)bh * N + qi] : 0.f;
-  const float nd = qi < N ? Dl[(size_t)bh * N + qi] : 0.f;  // -D
+  float l2, nd;  // LSE*log2(e) and -D of this lane's query
+  if constexpr (ROWS) {
+    // D = sum_d dO O over the row: 16-byte chunk p = kk*2 + g of the row is this lane's
+    // fragment kk (the other half of the row is in lane ^ 32).  Each chunk is one FMA chain in
+    // element order, then the chunks pair up as chunk p with chunk p ^ 2^m for m = 3, 2, 1
+    // (HD = 128) or 2, 1 (HD = 64), in this lane, and m = 0 with the partner lane: the
+    // preprocess kernel's shuffle tree, term for term.
+    u32x4 ofr[KST];
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) ofr[kk] = ld16_if(Oin + rowoff + kk * 16 + g * 8, qi < N);
+    float cs[KST];
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(TR::lo(ofr[kk][w]), TR::lo(of[kk][w]), acc);
+        acc = fmaf(TR::hi(ofr[kk][w]), TR::hi(of[kk][w]), acc);
+      }
+      cs[kk] = acc;
+    }
+#pragma unroll
+    for (int st = KST / 2; st >= 1; st >>= 1)
+#pragma unroll
+      for (int kk = 0; kk < st; ++kk) cs[kk] += cs[kk + st];
+    const float dsum = pair_sum(cs[0]);
+    l2 = qi < N ? LSEin[(size_t)bh * N + qi] * kLog2e : 0.f;
+    nd = qi < N ? -dsum : 0.f;
+    // one writer per query: group 0, key piece 0, the lane of the row's first half
+    if (qi < N && g == 0 && grp == 0 && (!PART || part == 0)) {
+      L2o[(size_t)bh * N + qi] = l2;
+      Dlo[(size_t)bh * N + qi] = nd;
+    }
+  } else {
+    l2 = qi < N ? L2[(size_t)bh * N + qi] : 0.f;
+    nd = qi < N ? Dl[(size_t)bh * N + qi] : 0.f;
+  }
   // On the large grids (one group per workgroup) every dP^T accumulator of a tile starts at -D
   // (all 16 registers of a lane hold its query's value), so the MFMAs yield dP^T - D directly
   // (dQ pass 1.8-2% faster there; the split-key workgroups measured 2-3% slower with it).
@@ -959,7 +1002,8 @@ hipError_t dkdv_hd(const BwdArgs& a) {
   return partial ? dkdv_t<TR, HD, false, true>(a) : dkdv_t<TR, HD, false, false>(a);
 }
 
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false, bool POST = false>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false, bool POST = false,
+          bool ROWS = false>
 hipError_t dq_nw(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
   constexpr int BR = NW / SPLIT * 32;
@@ -967,18 +1011,23 @@ hipError_t dq_nw(const BwdArgs& a) {
   const int n_kp = PART ? w.n_kp : 1;
   const long long blocks = a.B * a.Hq * (long long)n_qt * n_kp;
   float* const dqp = PART ? reinterpret_cast<float*>(a.ws + w.dq_part) : nullptr;
-  // (POST: the grouped-query dK/dV partial sums ride along, as in post_t)
+  // (POST: the grouped-query dK/dV partial sums ride along, as in post_t; ROWS: the pass forms
+  // the row values the preprocess would have stored, and stores them)
   const long long kv8 = POST ? a.B * a.Hkv * a.N * a.D / 8 : 0;
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT, PART, POST>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+  float* const lse2 = reinterpret_cast<float*>(a.ws + w.lse2);
+  float* const delta = reinterpret_cast<float*>(a.ws + w.delta);
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT, PART, POST, ROWS>), dim3((unsigned)blocks),
+                     dim3(NW * 64), 0, a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
-                     reinterpret_cast<const float*>(a.ws + w.lse2), reinterpret_cast<const float*>(a.ws + w.delta),
+                     ROWS ? nullptr : lse2, ROWS ? nullptr : delta,
                      static_cast<uint16_t*>(a.dq), (int)a.Hq, (int)a.Hkv, (int)a.N, n_qt, exp2_factor(a.scale),
                      a.scale, sign_bits(a.scale), (int)grid_fits(blocks, 8 / NW), n_kp, dqp,
                      POST ? reinterpret_cast<const float*>(a.ws + w.dk_part) : nullptr,
                      POST ? reinterpret_cast<const float*>(a.ws + w.dv_part) : nullptr,
                      POST ? static_cast<uint16_t*>(a.dk) : nullptr, POST ? static_cast<uint16_t*>(a.dv) : nullptr,
-                     (int)(a.Hq / a.Hkv) * w.n_qp, a.N * a.D / 8, kv8);
+                     (int)(a.Hq / a.Hkv) * w.n_qp, a.N * a.D / 8, kv8,
+                     ROWS ? static_cast<const uint16_t*>(a.o) : nullptr, ROWS ? a.lse : nullptr,
+                     ROWS ? lse2 : nullptr, ROWS ? delta : nullptr);
   if constexpr (PART) {
     FA_HIP_TRY(hipGetLastError());
     const long long n8 = a.B * a.Hq * a.N * a.D / 8;
@@ -994,23 +1043,33 @@ hipError_t dq_nw(const BwdArgs& a) {
 // the key range over two wave groups (causal grids, whose tiles carry uneven work, and grids
 // too small to give every CU two 4-wave workgroups), else 4-wave workgroups, two per CU.
 // With `post` (fa_bwd, when the dK/dV pass wrote partials) the pass also runs their sums
-// unless its grid takes key-range pieces; *fused says whether it did.
+// unless its grid takes key-range pieces; *fused says whether it did.  With `rows` (fa_bwd,
+// when the dK/dV pass writes no partials) the pass runs first and forms the row values itself.
+enum class DqMode { kPlain, kPost, kRows };
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false>
+hipError_t dq_mode(const BwdArgs& a, DqMode m) {
+  if constexpr (!PART)
+    if (m == DqMode::kPost) return dq_nw<TR, HD, CAUSAL, NW, SPLIT, false, true>(a);
+  if (m == DqMode::kRows) return dq_nw<TR, HD, CAUSAL, NW, SPLIT, PART, false, true>(a);
+  return dq_nw<TR, HD, CAUSAL, NW, SPLIT, PART>(a);
+}
 template <typename TR, int HD, bool CAUSAL>
-hipError_t dq_t(const BwdArgs& a, bool post, bool* fused) {
+hipError_t dq_t(const BwdArgs& a, DqMode m, bool* fused) {
   const long long big = a.B * a.Hq * ((a.N + 255) / 256);
-  *fused = post && bwd_key_pieces(a.B, a.Hq, a.N, a.D) == 1;
+  const bool pieces = bwd_key_pieces(a.B, a.Hq, a.N, a.D) > 1;
+  if (m == DqMode::kPost && pieces) m = DqMode::kPlain;
+  *fused = m == DqMode::kPost;
   if constexpr (HD == 128)
-    if (big >= 512) return *fused ? dq_nw<TR, HD, CAUSAL, 8, 1, false, true>(a) : dq_nw<TR, HD, CAUSAL, 8, 1>(a);
-  if (bwd_key_pieces(a.B, a.Hq, a.N, a.D) > 1) return dq_nw<TR, HD, CAUSAL, 8, 2, true>(a);
-  if (a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512)
-    return *fused ? dq_nw<TR, HD, CAUSAL, 8, 2, false, true>(a) : dq_nw<TR, HD, CAUSAL, 8, 2>(a);
-  return *fused ? dq_nw<TR, HD, CAUSAL, 4, 1, false, true>(a) : dq_nw<TR, HD, CAUSAL, 4, 1>(a);
+    if (big >= 512) return dq_mode<TR, HD, CAUSAL, 8, 1>(a, m);
+  if (pieces) return dq_mode<TR, HD, CAUSAL, 8, 2, true>(a, m);
+  if (a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512) return dq_mode<TR, HD, CAUSAL, 8, 2>(a, m);
+  return dq_mode<TR, HD, CAUSAL, 4, 1>(a, m);
 }
 
 template <typename TR>
-hipError_t dq_dt(const BwdArgs& a, bool post, bool* fused) {
-  if (a.D == 64) return a.causal ? dq_t<TR, 64, true>(a, post, fused) : dq_t<TR, 64, false>(a, post, fused);
-  return a.causal ? dq_t<TR, 128, true>(a, post, fused) : dq_t<TR, 128, false>(a, post, fused);
+hipError_t dq_dt(const BwdArgs& a, DqMode m, bool* fused) {
+  if (a.D == 64) return a.causal ? dq_t<TR, 64, true>(a, m, fused) : dq_t<TR, 64, false>(a, m, fused);
+  return a.causal ? dq_t<TR, 128, true>(a, m, fused) : dq_t<TR, 128, false>(a, m, fused);
 }
 
 template <typename TR>
@@ -1070,7 +1129,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a) {
 hipError_t launch_bwd_dq(const BwdArgs& a) {
   if (a.f32) return launch_bwd_dq_f32(a);
   bool fused = false;
-  return a.bf16 ? dq_dt<Bf16>(a, false, &fused) : dq_dt<F16>(a, false, &fused);
+  return a.bf16 ? dq_dt<Bf16>(a, DqMode::kPlain, &fused) : dq_dt<F16>(a, DqMode::kPlain, &fused);
 }
 
 hipError_t launch_bwd_dq_post(const BwdArgs& a) {
@@ -1078,10 +1137,15 @@ hipError_t launch_bwd_dq_post(const BwdArgs& a) {
     FA_HIP_TRY(launch_bwd_dq_f32(a));
     return launch_bwd_postprocess(a);
   }
-  const bool partial = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D).partial_dkdv;
+  const DqMode m = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D).partial_dkdv ? DqMode::kPost : DqMode::kPlain;
   bool fused = false;
-  FA_HIP_TRY(a.bf16 ? dq_dt<Bf16>(a, partial, &fused) : dq_dt<F16>(a, partial, &fused));
+  FA_HIP_TRY(a.bf16 ? dq_dt<Bf16>(a, m, &fused) : dq_dt<F16>(a, m, &fused));
   return fused ? hipSuccess : launch_bwd_postprocess(a);
+}
+
+hipError_t launch_bwd_dq_rows(const BwdArgs& a) {
+  bool fused = false;
+  return a.bf16 ? dq_dt<Bf16>(a, DqMode::kRows, &fused) : dq_dt<F16>(a, DqMode::kRows, &fused);
 }
 
 hipError_t launch_bwd_postprocess(const BwdArgs& a) {

@@ -82,6 +82,10 @@ hipError_t launch_bwd_dq(const BwdArgs& a);
 // The dQ pass followed by the postprocess, with the grouped-query dK/dV partial sums run inside
 // the dQ pass where its grid allows: the same results as launch_bwd_dq, launch_bwd_postprocess.
 hipError_t launch_bwd_dq_post(const BwdArgs& a);
+// The dQ pass forming and storing the row values (-D, LSE*log2(e)) itself, in place of the
+// preprocess launch before it: 16-bit tensors, and only where the dK/dV pass that follows
+// writes no partials.  The same results as launch_bwd_preprocess, launch_bwd_dq.
+hipError_t launch_bwd_dq_rows(const BwdArgs& a);
 hipError_t launch_bwd_postprocess(const BwdArgs& a);
 // The fp32 verification path (fa_f32.hip); launch_fwd and the launch_bwd_* stages dispatch to
 // these when FwdArgs::f32 / BwdArgs::f32 is set.

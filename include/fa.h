@@ -147,9 +147,11 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
  * Backward.  Inputs q, k, v, o (from fa_fwd), dout (dO, shape of q), lse (from fa_fwd);
  * outputs dq (shape of q), dk and dv (shape of k); all 16-bit tensors in `dtype`.
  * workspace: caller-owned device memory of at least fa_bwd_workspace_size(...) bytes,
- * contents undefined before and after.  Enqueues, in order, fa_bwd_preprocess,
- * fa_bwd_dkdv, fa_bwd_dq and fa_bwd_postprocess.  No atomics: every output element is
- * reduced in a fixed order, so the result is bitwise deterministic.
+ * contents undefined before and after.  Enqueues the stages below in the order
+ * fa_bwd_plan(...) names; where it runs fa_bwd_dq after fa_bwd_dkdv, the dQ pass also
+ * performs fa_bwd_postprocess's sums if its grid has no key-range pieces (one launch
+ * fewer, the same bits).  No atomics: every output element is reduced in a fixed order, so
+ * the result is bitwise deterministic.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -158,18 +160,35 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 /*
  * The stages of fa_bwd, exported so a caller (or a profiler harness) can place events
- * between them.  Running them in this order on one stream with the same workspace is
- * exactly fa_bwd (fa_bwd_dkdv and fa_bwd_dq only depend on the preprocess and may run in
- * either order).
+ * between them.  Running them on one stream with the same workspace, in the order
+ * fa_bwd_plan(...) gives, enqueues exactly fa_bwd's kernels (apart from the postprocess
+ * fa_bwd folds into its dQ pass) and gives its bits; the order fa_bwd_preprocess,
+ * fa_bwd_dkdv, fa_bwd_dq, fa_bwd_postprocess gives the same bits for every problem
+ * (fa_bwd_dkdv and fa_bwd_dq only depend on the row values and may run in either order).
  *   fa_bwd_preprocess:  -D = -rowsum(dout * o) and LSE * log2(e) into the workspace (fp32).
  *   fa_bwd_dkdv:        key-stationary pass: recomputes P from the workspace's LSE and
- *                       writes dk = scale * dS^T Q and dv = P^T dO (Hq == Hkv), or fp32
- *                       per-query-head partials into the workspace (Hq > Hkv).
+ *                       writes dk = scale * dS^T Q and dv = P^T dO, or fp32 partials into the
+ *                       workspace (Hq > Hkv, or grids cut into query-range pieces).
  *   fa_bwd_dq:          query-stationary pass: recomputes P and dS and writes
  *                       dq = scale * dS K.
- *   fa_bwd_postprocess: for Hq > Hkv, sums the dK/dV partials over each query-head group into
- *                       dk/dv; for Hq == Hkv it enqueues nothing.
+ *   fa_bwd_dq_rows:     fa_bwd_preprocess and fa_bwd_dq as one pass: each query row's -D and
+ *                       LSE * log2(e) are formed from o, dout and lse where the dQ pass holds
+ *                       the row, stored into the workspace with the bits fa_bwd_preprocess
+ *                       stores, and used there; then dq is written.  It may take the place of
+ *                       the two in any order above (for FA_FP32 it enqueues the two).
+ *   fa_bwd_postprocess: sums the dK/dV partials (over each query-head group and query-range
+ *                       piece) into dk/dv; where fa_bwd_dkdv wrote dk/dv it enqueues nothing.
  */
+enum fa_bwd_plan_kind {
+  FA_BWD_PLAN_STAGES = 0, /* fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_postprocess */
+  FA_BWD_PLAN_ROWS = 1    /* fa_bwd_dq_rows, fa_bwd_dkdv */
+};
+/*
+ * The order fa_bwd enqueues for a problem: FA_BWD_PLAN_ROWS for 16-bit tensors whose dK/dV
+ * pass writes dk and dv directly (the dQ pass goes first and forms the row values, one launch
+ * fewer), else FA_BWD_PLAN_STAGES.  For arguments fa_bwd would reject, the negated status.
+ */
+int fa_bwd_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype);
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
                       size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
                       int dtype, void* stream);
@@ -179,6 +198,10 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, v
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
               void* workspace, size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
               int64_t D, float softmax_scale, int causal, int dtype, void* stream);
+int fa_bwd_dq_rows(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* workspace, size_t workspace_bytes, int64_t B,
+                   int64_t Hq, int64_t Hkv, int64_t N, int64_t D, float softmax_scale, int causal,
+                   int dtype, void* stream);
 int fa_bwd_postprocess(void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int dtype,
                        void* stream);

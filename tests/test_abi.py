@@ -179,6 +179,49 @@ def test_stage_entry_points_reject(lib):
         STATUS["FA_ERR_ALIAS"]
 
 
+def test_bwd_plan(lib):
+    ROWS, STAGES = fa.FA_BWD_PLAN_ROWS, fa.FA_BWD_PLAN_STAGES
+    text = open(HEADER).read()
+    assert re.search(rf"\bFA_BWD_PLAN_STAGES\s*=\s*{STAGES}\b", text)
+    assert re.search(rf"\bFA_BWD_PLAN_ROWS\s*=\s*{ROWS}\b", text)
+    # MHA grids whose dK/dV pass writes dk/dv directly: the dQ pass first, forming the row values
+    assert fa.fa_bwd_plan(1, 16, 16, 16384, 128, fa.FA_BF16) == ROWS
+    assert fa.fa_bwd_plan(4, 16, 16, 4096, 128, fa.FA_BF16) == ROWS
+    assert fa.fa_bwd_plan(1, 2, 2, 256, 64, fa.FA_FP16) == ROWS
+    # partials: grouped-query heads, or one head cut into query-range pieces
+    assert fa.fa_bwd_plan(1, 16, 4, 4096, 128, fa.FA_FP16) == STAGES
+    assert fa.fa_bwd_plan(1, 1, 1, 16384, 128, fa.FA_BF16) == STAGES
+    # the fp32 path keeps the four stages
+    assert fa.fa_bwd_plan(1, 16, 16, 4096, 128, fa.FA_FP32) == STAGES
+    # invalid arguments: the negated status
+    assert lib.fa_bwd_plan(1, 16, 16, 4096, 96, 1) == -STATUS["FA_ERR_HEAD_DIM"]
+    assert lib.fa_bwd_plan(1, 16, 16, 4096, 128, 5) == -STATUS["FA_ERR_DTYPE"]
+    assert lib.fa_bwd_plan(0, 16, 16, 4096, 128, 1) == -STATUS["FA_ERR_BAD_SHAPE"]
+    with pytest.raises(RuntimeError, match="head"):
+        fa.fa_bwd_plan(1, 16, 16, 4096, 96, fa.FA_BF16)
+
+
+def test_dq_rows_rejects(lib):
+    B, Hq, Hkv, N, D = 1, 4, 4, 100, 128
+    need = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D)
+
+    def rows(ws_bytes=need, scale=0.1, dtype=1, Dh=D, **over):
+        names = ["q", "k", "v", "o", "do", "lse", "dq", "ws"]
+        ptrs = {n: ptr(i) for i, n in enumerate(names)}
+        ptrs.update(over)
+        return lib.fa_bwd_dq_rows(*[ptrs[n] for n in names], ws_bytes, B, Hq, Hkv, N, Dh, scale, 1, dtype, None)
+    assert rows(ws_bytes=need - 1) == STATUS["FA_ERR_WORKSPACE"]
+    assert rows(Dh=80) == STATUS["FA_ERR_HEAD_DIM"]
+    assert rows(dtype=4) == STATUS["FA_ERR_DTYPE"]
+    assert rows(scale=float("nan")) == STATUS["FA_ERR_SCALE"]
+    assert rows(o=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]
+    assert rows(lse=ctypes.c_void_p(0)) == STATUS["FA_ERR_NULL_POINTER"]
+    assert rows(lse=ctypes.c_void_p(A + 2)) == STATUS["FA_ERR_ALIGNMENT"]
+    assert rows(dq=ptr(3)) == STATUS["FA_ERR_ALIAS"]   # dq over o
+    assert rows(ws=ptr(5)) == STATUS["FA_ERR_ALIAS"]   # the workspace over lse
+    assert rows(scale=-0.1, dq=ptr(0)) == STATUS["FA_ERR_ALIAS"]  # a negative scale passes
+
+
 def test_splitkv_workspace_and_parts(lib):
     B, Hq, Hkv, N, D = 1, 2, 1, 3000, 128
     up = lambda x: (x + 255) // 256 * 256

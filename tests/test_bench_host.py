@@ -79,6 +79,12 @@ def test_workloads_and_bytes():
     q = 16 * 16384 * 128 * 2
     assert b["fwd"] == 4 * q + 4 * 16 * 16384
     assert b["bwd_dkdv"] == 6 * q + 8 * 16 * 16384
+    # fa_bwd's plan for this workload: the dQ pass forms the row values (it also reads O and the
+    # LSE and writes -D and LSE*log2 e), and there is no preprocess launch
+    assert bench.rows_first_plan(s)
+    r = bench.algorithmic_bytes(s, rows_first=True)
+    assert r["bwd_dq"] == 6 * q + 12 * 16 * 16384 and "bwd_preprocess" not in r
+    assert not bench.rows_first_plan(WORKLOADS["gqa_causal_fp16"][0])
     assert bench.flops(s) == pytest.approx(7696.58e9, rel=1e-5)
 
 

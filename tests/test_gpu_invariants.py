@@ -172,6 +172,14 @@ STAGE_SHAPES = [
     (1, 16, 4, 2048, 128, "fp16", True),   # one-round causal grid: the dQ pass runs the sums
     (2, 16, 4, 4096, 128, "bf16", False),  # 256-query dQ workgroups with the sums
     (2, 16, 4, 4096, 64, "fp16", False),   # 4-wave dQ workgroups (two per CU) with the sums
+    # no dK/dV partials: the dQ pass runs first and forms the row values itself
+    (2, 16, 16, 4096, 128, "bf16", False),  # 256-query dQ workgroups
+    (1, 32, 32, 4096, 128, "fp16", True),   # 256-query dQ workgroups, causal
+    (1, 16, 16, 2000, 128, "bf16", True),   # split 128-query workgroups, ragged tail
+    (2, 16, 16, 2048, 64, "fp16", False),   # 4-wave dQ workgroups
+    (4, 16, 16, 1000, 128, "bf16", False),  # 4-wave dQ workgroups, D=128, ragged tail
+    (1, 2, 2, 512, 64, "fp16", False),      # dQ key-range pieces (the first piece stores the rows)
+    (1, 2, 2, 256, 64, "fp16", True),       # the tiny causal workload
 ]
 
 
@@ -179,7 +187,9 @@ STAGE_SHAPES = [
                                                     for b, hq, hk, n, d, t, cz in STAGE_SHAPES])
 def test_backward_stages_equal_fused_call(torch_fa, dims):
     """The exported stages, run in order on one stream, reproduce fa_bwd bit for bit (fa_bwd
-    runs the grouped-query partial sums inside its dQ pass where the grid allows)."""
+    runs the grouped-query partial sums inside its dQ pass where the grid allows, and where
+    the dK/dV pass writes no partials it runs the dQ pass first, forming the preprocess's row
+    values there)."""
     torch, fa = torch_fa
     from exact_attention_fa_amd.inputs import Shape
     shape = Shape(*dims)
@@ -195,6 +205,17 @@ def test_backward_stages_equal_fused_call(torch_fa, dims):
     fa.fa_bwd_postprocess(dk2, dv2, ws, Hq)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    # the combined stage in place of the preprocess and the dQ pass (fa_bwd's own order where
+    # fa_bwd_plan says so), on a workspace that holds the last run's values
+    plan = fa.fa_bwd_plan(B, Hq, Hkv, N, D, fa.FA_BF16 if q.dtype == torch.bfloat16 else fa.FA_FP16)
+    assert plan == (fa.FA_BWD_PLAN_ROWS if Hq == Hkv else fa.FA_BWD_PLAN_STAGES), plan
+    dq3, dk3, dv3 = (torch.full_like(t, float("nan")) for t in (dq, dk, dv))
+    ws.fill_(0xFF)
+    fa.fa_bwd_dq_rows(q, k, v, o, do, lse, dq3, ws, causal=causal)
+    fa.fa_bwd_dkdv(q, k, v, do, dk3, dv3, ws, causal=causal)
+    fa.fa_bwd_postprocess(dk3, dv3, ws, Hq)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
 
 
 def test_concurrent_streams_match_one_stream(torch_fa):
