@@ -116,3 +116,31 @@ def test_f32_splitkv_runs_as_fwd():
     o2, l2 = fa.fa_fwd_splitkv(q, k, v, n_split=4, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_f32_stage_orders_match_fa_bwd():
+    """The fp32 path's stages, in either order (the four stages; fa_bwd_dq_rows, which on this
+    path enqueues the preprocess and the dQ pass, then the dK/dV pass), give fa_bwd's bits."""
+    import torch
+    import exact_attention_fa_amd as fa
+    shape = Shape(1, 4, 2, 333, 128, "fp32", True)
+    q, k, v, do = (x.cuda() for x in make_inputs(shape, seed=515))
+    B, Hq, Hkv, N, D = shape.B, shape.Hq, shape.Hkv, shape.N, shape.D
+    assert fa.fa_bwd_plan(B, Hq, Hkv, N, D, fa.FA_FP32) == fa.FA_BWD_PLAN_STAGES
+    o, lse = fa.fa_fwd(q, k, v, causal=True)
+    ref = fa.fa_bwd(q, k, v, o, do, lse, causal=True)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D), dtype=torch.uint8, device="cuda")
+    for rows in (False, True):
+        dq, dk, dv = (torch.full_like(t, float("nan")) for t in ref)
+        ws.fill_(0xFF)
+        if rows:
+            fa.fa_bwd_dq_rows(q, k, v, o, do, lse, dq, ws, causal=True)
+            fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=True)
+        else:
+            fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
+            fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=True)
+            fa.fa_bwd_dq(q, k, v, do, dq, ws, causal=True)
+        fa.fa_bwd_postprocess(dk, dv, ws, Hq)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            assert torch.equal(a, b), (rows, name)
