@@ -138,8 +138,10 @@ int fa_merge_partials(const float* o_parts, const float* lse_parts, int n_parts,
 
 /*
  * Bytes of device workspace fa_bwd needs: the fp32 D = rowsum(dO * O) and LSE * log2(e)
- * vectors and, when Hq > Hkv, fp32 per-query-head dK/dV partials.  Returns 0 for invalid
- * shapes.
+ * vectors; fp32 dK/dV partials per query head and query-range piece when Hq > Hkv or the
+ * grid is cut into query-range pieces; fp32 dQ partials per key-range piece when the dQ
+ * pass's grid is cut into such pieces (grids too small to fill the GPU).  Returns 0 for
+ * invalid shapes.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D);
 
