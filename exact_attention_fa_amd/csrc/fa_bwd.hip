@@ -491,9 +491,10 @@ __device__ FA_INL void post_dkdv_item(long long i, const float* __restrict__ dKp
 }
 
 // ---------------------------------------------------------------- dQ
-// Query-stationary: a workgroup owns 128 or 256 query rows (32 per wave) of one head and streams
-// 32-key tiles of K and V of its KV head through LDS (direct loads issued three tiles ahead;
-// four K buffers, three V buffers; one barrier per tile).  Per tile j, per wave:
+// Query-stationary: a workgroup owns 64, 128 or 256 query rows (32 per wave) of one head and
+// streams 32-key tiles of K and V of its KV head through LDS (direct loads issued DIST tiles
+// ahead into DIST + 1 K buffers and DIST V buffers, DIST = 3, or 2 where two workgroups of
+// D = 128 share a CU; one barrier per tile).  Per tile j, per wave:
 //   S^T = K Q^T and dP^T = V dO^T  (K, V rows from LDS; Q and dO fragments in registers)
 //   dS^T = exp2(S^T c2 - LSE log2 e) * (dP^T - D)        (fp32, one query per lane)
 //   dQ^T += K^T dS^T  (K^T read transposed from the K tile; the rounded dS^T registers are
@@ -516,7 +517,7 @@ __device__ FA_INL void post_dkdv_item(long long i, const float* __restrict__ dKp
 // launch.  The sum runs in the preprocess kernel's order (the same per-16-byte FMA chains, the
 // same pairwise tree), so both routes give the same bits.  (fa_bwd runs the dQ pass first this
 // way wherever the dK/dV pass writes no partials.)
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART, bool SUMS, bool ROWS>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART, bool SUMS, bool ROWS, int DIST>
 __global__ void __launch_bounds__(NW * 64, 8 / NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -536,7 +537,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int TILE = BC * HD * 2;         // bytes of one K or V tile
   constexpr int TI = TILE / 1024 / GW;      // 1 KB direct loads per wave per tile
   static_assert(TI * 1024 * GW == TILE, "tile must split into 1 KB loads over the waves");
-  constexpr int NK = 4, NV = 3;             // K tiles j..j+3, V tiles j+1..j+3
+  static_assert(DIST == 2 || DIST == 3, "loads two or three tiles ahead");
+  constexpr int NK = DIST + 1, NV = DIST;  // K tiles j..j+DIST, V tiles j+1..j+DIST
   constexpr int RD = 4;                     // LDS operand reads issued this many MFMAs ahead
 
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * (NK + NV) * TILE];
@@ -602,9 +604,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   char* const kb0 = smem + grp * ((NK + NV) * TILE);  // K buffers kb0 + i*TILE, i < NK
   char* const vb0 = kb0 + NK * TILE;                   // V buffers vb0 + i*TILE, i < NV
-  // the group's tiles 0, 1, 2 go to K buffers 0, 1, 2 and V buffers 0, 1, 2
+  // the group's tiles t < DIST go to K buffer t and V buffer t
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
+  for (int t = 0; t < DIST; ++t)
     if (t < Tg) issue(t, kb0 + t * TILE, vb0 + t * TILE);
 
   // B operands: slot j of k-step kk = Q[qi][kk*16 + g*8 + j] and dO[qi][...]
@@ -742,9 +744,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // Step j (0 <= j < T): wait for tile j+1 (tile j+2 may stay in flight), let every wave see
-  // it (everyone is then also done with step j-1, whose buffers the next loads refill), load
-  // tile j+3, then [S^T/dP^T of tile j+1 | dS^T of tile j] and dQ of tile j.  (cs, cdp) hold
+  // Step j (0 <= j < T): wait for tile j+1 (with DIST = 3, tile j+2 may stay in flight), let
+  // every wave see it (everyone is then also done with step j-1, whose buffers the next loads
+  // refill), load tile j+DIST, then [S^T/dP^T of tile j+1 | dS^T of tile j] and dQ of tile j.  (cs, cdp) hold
   // tile j's S^T/dP^T, (ns, ndp) receive tile j+1's.  The LDS buffers are restrict-qualified
   // parameters so that the compiler can tell these reads from the loads in flight.
   enum Kind { kSteady, kLast, kLastMasked, kIdle };
@@ -752,13 +754,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   const char* __restrict__ nV, char* __restrict__ dK_, char* __restrict__ dV_, f32x16& cs,
                   f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
     constexpr Kind KIND = decltype(kind_tag)::value;
-    if (j + 2 < Tg)
+    if (DIST == 3 && j + 2 < Tg)
       wait_vmcnt<2 * TI>();
     else
       wait_vmcnt<0>();
     dma_barrier();
     if constexpr (KIND != kSteady)
-      if (j + 3 < Tg) issue(j + 3, dK_, dV_);
+      if (j + DIST < Tg) issue(j + DIST, dK_, dV_);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 dsb[2];
     float dt;
@@ -768,7 +770,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       ndp = ndv;
       // the next tile's loads go out under the first MFMAs
       sdp(std::true_type{}, nK, nV, ns, ndp, [&](int i) FA_INL {
-        if (i == 1 && j + 3 < Tg) issue(j + 3, dK_, dV_);
+        if (i == 1 && j + DIST < Tg) issue(j + DIST, dK_, dV_);
 #pragma unroll
         for (int w = 0; w < 16; ++w)
           if (w * 2 * KST / 16 == i) ds_unit(std::false_type{}, j, cs, cdp, dsb, dt, w);
@@ -781,34 +783,32 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // Buffer rings: K tiles j, j+1, j+2 and the slot for j+3; V tiles j+1, j+2 and the slot
-  // for j+3.
-  char* k0 = kb0;
-  char* k1 = kb0 + TILE;
-  char* k2 = kb0 + 2 * TILE;
-  char* k3 = kb0 + 3 * TILE;
-  char* v1 = vb0 + TILE;
-  char* v2 = vb0 + 2 * TILE;
-  char* v3 = vb0;
+  // Buffer rings: kr = K tiles j .. j+DIST-1 and the slot for j+DIST; vr = V tiles
+  // j+1 .. j+DIST-1 and the slot for j+DIST (tile 0's V buffer, free after the prologue).
+  char* kr[NK];
+  char* vr[NV];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) kr[i] = kb0 + i * TILE;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) vr[i] = vb0 + ((i + 1) % NV) * TILE;
   f32x16 sa, dpa, sb, dpb;
   auto run = [&](auto kind_tag, int j, f32x16& cs, f32x16& cdp, f32x16& ns, f32x16& ndp) FA_INL {
-    step(kind_tag, j, k0, k1, v1, k3, v3, cs, cdp, ns, ndp);
-    char* t = k0;
-    k0 = k1;
-    k1 = k2;
-    k2 = k3;
-    k3 = t;
-    t = v1;
-    v1 = v2;
-    v2 = v3;
-    v3 = t;
+    step(kind_tag, j, kr[0], kr[1], vr[0], kr[NK - 1], vr[NV - 1], cs, cdp, ns, ndp);
+    char* const t = kr[0];
+#pragma unroll
+    for (int i = 0; i + 1 < NK; ++i) kr[i] = kr[i + 1];
+    kr[NK - 1] = t;
+    char* const u = vr[0];
+#pragma unroll
+    for (int i = 0; i + 1 < NV; ++i) vr[i] = vr[i + 1];
+    vr[NV - 1] = u;
   };
   using KSteady = std::integral_constant<Kind, kSteady>;
   using KLast = std::integral_constant<Kind, CAUSAL ? kLastMasked : kLast>;
   using KIdle = std::integral_constant<Kind, kIdle>;
 
-  // prologue: tile 0 resident (tiles 1 and 2 may stay in flight), S^T/dP^T of tile 0
-  if (Tg > 2)
+  // prologue: tile 0 resident (tiles 1 .. DIST-1 may stay in flight), S^T/dP^T of tile 0
+  if (DIST == 3 && Tg > 2)
     wait_vmcnt<4 * TI>();
   else if (Tg > 1)
     wait_vmcnt<2 * TI>();
@@ -1003,7 +1003,7 @@ hipError_t dkdv_hd(const BwdArgs& a) {
 }
 
 template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false, bool POST = false,
-          bool ROWS = false>
+          bool ROWS = false, int DIST = 3>
 hipError_t dq_nw(const BwdArgs& a) {
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.Hq, a.Hkv, a.N, a.D);
   constexpr int BR = NW / SPLIT * 32;
@@ -1016,7 +1016,7 @@ hipError_t dq_nw(const BwdArgs& a) {
   const long long kv8 = POST ? a.B * a.Hkv * a.N * a.D / 8 : 0;
   float* const lse2 = reinterpret_cast<float*>(a.ws + w.lse2);
   float* const delta = reinterpret_cast<float*>(a.ws + w.delta);
-  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT, PART, POST, ROWS>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((bwd_dq_kernel<TR, HD, CAUSAL, NW, SPLIT, PART, POST, ROWS, DIST>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
                      ROWS ? nullptr : lse2, ROWS ? nullptr : delta,
@@ -1041,17 +1041,20 @@ hipError_t dq_nw(const BwdArgs& a) {
 // query, which lowers the power the pass draws and lets the clock rise; D = 64 tiles are too
 // small to split over 8 waves.  Smaller grids use 128-query tiles: 8-wave workgroups that split
 // the key range over two wave groups (causal grids, whose tiles carry uneven work, and grids
-// too small to give every CU two 4-wave workgroups), else 4-wave workgroups, two per CU.
+// too small to give every CU two 4-wave workgroups), else 4-wave workgroups, two per CU.  A
+// causal grid that runs in one round takes 64-query tiles, split over two groups of two waves,
+// two workgroups per CU (at D = 128 with loads two tiles ahead, so that two fit the LDS): its
+// causal_tile order hands every CU a heavy and a light tile.
 // With `post` (fa_bwd, when the dK/dV pass wrote partials) the pass also runs their sums
 // unless its grid takes key-range pieces; *fused says whether it did.  With `rows` (fa_bwd,
 // when the dK/dV pass writes no partials) the pass runs first and forms the row values itself.
 enum class DqMode { kPlain, kPost, kRows };
-template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false>
+template <typename TR, int HD, bool CAUSAL, int NW, int SPLIT, bool PART = false, int DIST = 3>
 hipError_t dq_mode(const BwdArgs& a, DqMode m) {
   if constexpr (!PART)
-    if (m == DqMode::kPost) return dq_nw<TR, HD, CAUSAL, NW, SPLIT, false, true>(a);
-  if (m == DqMode::kRows) return dq_nw<TR, HD, CAUSAL, NW, SPLIT, PART, false, true>(a);
-  return dq_nw<TR, HD, CAUSAL, NW, SPLIT, PART>(a);
+    if (m == DqMode::kPost) return dq_nw<TR, HD, CAUSAL, NW, SPLIT, false, true, false, DIST>(a);
+  if (m == DqMode::kRows) return dq_nw<TR, HD, CAUSAL, NW, SPLIT, PART, false, true, DIST>(a);
+  return dq_nw<TR, HD, CAUSAL, NW, SPLIT, PART, false, false, DIST>(a);
 }
 template <typename TR, int HD, bool CAUSAL>
 hipError_t dq_t(const BwdArgs& a, DqMode m, bool* fused) {
@@ -1062,6 +1065,8 @@ hipError_t dq_t(const BwdArgs& a, DqMode m, bool* fused) {
   if constexpr (HD == 128)
     if (big >= 512) return dq_mode<TR, HD, CAUSAL, 8, 1>(a, m);
   if (pieces) return dq_mode<TR, HD, CAUSAL, 8, 2, true>(a, m);
+  if constexpr (CAUSAL)
+    if (grid_fits(a.B * a.Hq * ((a.N + 63) / 64), 2)) return dq_mode<TR, HD, CAUSAL, 4, 2, false, HD == 128 ? 2 : 3>(a, m);
   if (a.causal || a.B * a.Hq * ((a.N + 127) / 128) < 512) return dq_mode<TR, HD, CAUSAL, 8, 2>(a, m);
   return dq_mode<TR, HD, CAUSAL, 4, 1>(a, m);
 }
