@@ -746,9 +746,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // Step j (0 <= j < T): wait for tile j+1 (with DIST = 3, tile j+2 may stay in flight), let
   // every wave see it (everyone is then also done with step j-1, whose buffers the next loads
-  // refill), load tile j+DIST, then [S^T/dP^T of tile j+1 | dS^T of tile j] and dQ of tile j.  (cs, cdp) hold
-  // tile j's S^T/dP^T, (ns, ndp) receive tile j+1's.  The LDS buffers are restrict-qualified
-  // parameters so that the compiler can tell these reads from the loads in flight.
+  // refill), load tile j+DIST, then [S^T/dP^T of tile j+1 | dS^T of tile j] and dQ of tile j.
+  // (cs, cdp) hold tile j's S^T/dP^T, (ns, ndp) receive tile j+1's.  The LDS buffers are
+  // restrict-qualified parameters so that the compiler can tell these reads from the loads in
+  // flight.
   enum Kind { kSteady, kLast, kLastMasked, kIdle };
   auto step = [&](auto kind_tag, const int j, const char* __restrict__ tK, const char* __restrict__ nK,
                   const char* __restrict__ nV, char* __restrict__ dK_, char* __restrict__ dV_, f32x16& cs,
