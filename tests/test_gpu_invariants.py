@@ -218,6 +218,35 @@ def test_backward_stages_equal_fused_call(torch_fa, dims):
     assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
 
 
+@pytest.mark.parametrize("scale", [-0.15, 0.0])
+def test_backward_stage_orders_other_scales(torch_fa, scale):
+    """Both stage orders reproduce fa_bwd bit for bit at a negative and a zero softmax scale
+    (MHA: fa_bwd forms the row values in its dQ pass; GQA: the preprocess runs first)."""
+    torch, fa = torch_fa
+    from exact_attention_fa_amd.inputs import Shape
+    for dims in [(1, 8, 8, 1500, 128, "bf16", True), (1, 8, 2, 900, 64, "fp16", False)]:
+        shape = Shape(*dims)
+        B, Hq, Hkv, N, D, causal = shape.B, shape.Hq, shape.Hkv, shape.N, shape.D, shape.causal
+        q, k, v, do = inputs(shape, 29)
+        o, lse = fa.fa_fwd(q, k, v, causal=causal, softmax_scale=scale)
+        ref = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, softmax_scale=scale)
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D), dtype=torch.uint8, device="cuda")
+        for rows in (False, True):
+            dq, dk, dv = (torch.full_like(t, float("nan")) for t in ref)
+            ws.fill_(0xFF)
+            if rows:
+                fa.fa_bwd_dq_rows(q, k, v, o, do, lse, dq, ws, causal=causal, softmax_scale=scale)
+                fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=causal, softmax_scale=scale)
+            else:
+                fa.fa_bwd_preprocess(o, do, lse, ws, Hkv)
+                fa.fa_bwd_dkdv(q, k, v, do, dk, dv, ws, causal=causal, softmax_scale=scale)
+                fa.fa_bwd_dq(q, k, v, do, dq, ws, causal=causal, softmax_scale=scale)
+            fa.fa_bwd_postprocess(dk, dv, ws, Hq)
+            torch.cuda.synchronize()
+            for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+                assert torch.equal(a, b), (dims, scale, rows, name)
+
+
 def test_concurrent_streams_match_one_stream(torch_fa):
     """The library keeps no mutable global state: the same calls enqueued on two streams at
     once (separate outputs and workspaces) give the bits of a single-stream run."""
