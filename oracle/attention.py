@@ -24,7 +24,7 @@ float64 with NumPy, with no tiling, no online rescaling and no fusion:
   dot product of dO and O) and dQ = scale * dS K, dK = scale * dS^T Q follow
   from the chain rule; finite differences pin them in the tests.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * ``scale`` multiplies Q K^T before the softmax; the log-sum-exp (LSE) is the
   natural-log log-sum-exp of the *scaled* scores over the visible keys.
