@@ -539,7 +539,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   static_assert(TI * 1024 * GW == TILE, "tile must split into 1 KB loads over the waves");
   static_assert(DIST == 2 || DIST == 3, "loads two or three tiles ahead");
   constexpr int NK = DIST + 1, NV = DIST;  // K tiles j..j+DIST, V tiles j+1..j+DIST
-  constexpr int RD = 4;                     // LDS operand reads issued this many MFMAs ahead
+  constexpr int RD = 3;                     // LDS operand reads issued this many MFMAs ahead
 
   __shared__ __attribute__((aligned(1024))) char smem[SPLIT * (NK + NV) * TILE];
 
