@@ -198,7 +198,7 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   //      MFMAs of P_{j-1} V_{j-1} run, so the exp2 work hides under matrix work.  Each MFMA
   //      is fenced together with a fixed share of the VALU work (and, once per fragment, the
   //      LDS read of the operand RD fragments ahead), so the two pipes stay interleaved.
-  constexpr int RD = 4;
+  constexpr int RD = 5;
   // K fragment i (i = kb*KST + kk): key rows kb*32.., head-dim k-step kk.
   auto kfrag = [&](const char* tK, int i) FA_INL {
     const int kk = i % KST, kb = i / KST;
