@@ -594,13 +594,19 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     sl_pos_to_rc<BC>((uint32_t)((wv * TI + r) * 64 + lane), row, col);
     kvo[r] = (uint32_t)(row * HD + col) * 2u;
   }
-  auto issue = [&](int t, char* dK_, char* dV_) FA_INL {
+  auto issue_k = [&](int t, char* dK_) FA_INL {
 #pragma unroll
-    for (int r = 0; r < TI; ++r) {
-      const int blk = wv * TI + r;
-      dma_to_lds<16>(rK, kvo[r], (uint32_t)(t0 + t) * (BC * HD * 2), dK_ + blk * 1024);
-      dma_to_lds<16>(rV, kvo[r], (uint32_t)(t0 + t) * (BC * HD * 2), dV_ + blk * 1024);
-    }
+    for (int r = 0; r < TI; ++r)
+      dma_to_lds<16>(rK, kvo[r], (uint32_t)(t0 + t) * (BC * HD * 2), dK_ + (wv * TI + r) * 1024);
+  };
+  auto issue_v = [&](int t, char* dV_) FA_INL {
+#pragma unroll
+    for (int r = 0; r < TI; ++r)
+      dma_to_lds<16>(rV, kvo[r], (uint32_t)(t0 + t) * (BC * HD * 2), dV_ + (wv * TI + r) * 1024);
+  };
+  auto issue = [&](int t, char* dK_, char* dV_) FA_INL {
+    issue_k(t, dK_);
+    issue_v(t, dV_);
   };
   char* const kb0 = smem + grp * ((NK + NV) * TILE);  // K buffers kb0 + i*TILE, i < NK
   char* const vb0 = kb0 + NK * TILE;                   // V buffers vb0 + i*TILE, i < NV
@@ -769,9 +775,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if constexpr (KIND == kSteady) {
       ns = f32x16{};
       ndp = ndv;
-      // the next tile's loads go out under the first MFMAs
+      // the next tile's loads go out under the first MFMAs (K after the first, V after the third:
+      // 0.3-0.7% faster than both after the second)
       sdp(std::true_type{}, nK, nV, ns, ndp, [&](int i) FA_INL {
-        if (i == 1 && j + DIST < Tg) issue(j + DIST, dK_, dV_);
+        if (i == 0 && j + DIST < Tg) issue_k(j + DIST, dK_);
+        if (i == 2 && j + DIST < Tg) issue_v(j + DIST, dV_);
 #pragma unroll
         for (int w = 0; w < 16; ++w)
           if (w * 2 * KST / 16 == i) ds_unit(std::false_type{}, j, cs, cdp, dsb, dt, w);

@@ -514,7 +514,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       scale_acc();
       need = false;
     }
-    // The steady steps issue the next tiles' loads under their first S MFMAs.
+    // The steady steps issue the next tiles' loads under their first S MFMAs (K after the first,
+    // V after the third: 0.5-1% faster than after the second and fourth, and than any later pair).
     constexpr bool LATE_ISSUE = KIND == kSteady || KIND == kSteadyMasked;
     if constexpr (!LATE_ISSUE) {
       if (j + DIST < Tg) issue(rK, j + DIST, nK);
@@ -536,8 +537,8 @@ fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       constexpr int NSM = 2 * KST * QB, NPV = DB * 4 * QB, FIRST = kSmExp0, NP = 16 * QB;
       u32x4 vpre[RD];
       auto packs = [&](int i) FA_INL {
-        if (i == 1 && j + DIST < Tg) issue(rK, j + DIST, nK);
-        if (i == 3 && j + DIST - 1 < Tg) issue(rV, j + DIST - 1, nV);
+        if (i == 0 && j + DIST < Tg) issue(rK, j + DIST, nK);
+        if (i == 2 && j + DIST - 1 < Tg) issue(rV, j + DIST - 1, nV);
 #pragma unroll
         for (int u = 0; u < NP; ++u)
           if (u * NSM / NP == i) pack_unit(pb, u);
