@@ -4,6 +4,7 @@ table and its algorithmic byte counts."""
 import ast
 import os
 import subprocess
+import sys
 
 import pytest
 
@@ -122,3 +123,13 @@ def test_traffic_summary_scales_by_copy(tmp_path, capsys):
     alg = bench.algorithmic_bytes(WORKLOADS["fwd_bf16_long"][1])["bwd_dkdv"]
     assert f"algorithmic_bytes_per_launch = {alg}" in out
     assert f"source_sha256_16 = {bench.source_hash('bwd_dkdv')}" in out
+
+
+@pytest.mark.parametrize("env, argv", [({}, ["--gpus", "2"]), ({"WORLD_SIZE": "4"}, [])])
+def test_more_than_one_gpu_is_refused(env, argv):
+    """More than one GPU (a flag, or a launcher's WORLD_SIZE) exits with status 2 and says why,
+    before touching torch's device state."""
+    e = dict(os.environ, **env)
+    p = subprocess.run([sys.executable, bench.__file__, *argv], capture_output=True, text=True, env=e, timeout=120)
+    assert p.returncode == 2, p.stderr[-500:]
+    assert "measures one GPU" in p.stderr and p.stdout == ""
